@@ -1,0 +1,145 @@
+"""ctypes binding for ``libattn.so`` (C ABI in ``include/attn.h``).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and the current HIP stream are passed to the
+C entry point of the same name, and a non-zero status becomes ``AttnError``.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn.so"
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {attn_status_str(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libattn.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.tra_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
+    lib.tra_fwd.restype = ci
+    lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
+    lib.tra_fwd_f32.restype = ci
+    lib.nsa_sel_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.nsa_sel_fwd.restype = ci
+    lib.attn_status_str.argtypes = [ci]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _tra(fn_name: str, dtype, q, k, v, beta, p, out, stream):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dtype)
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must all be [B, H, T, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape")
+    B, H, T, D = q.shape
+    fn = getattr(load_library(), fn_name)
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            B, H, T, D, float(beta), float(p), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError(fn_name, rc)
+    return out
+
+
+def tra_fwd(q, k, v, beta, p, out=None, stream=None):
+    """Threshold Rectified Attention forward, bf16 in / bf16 out, fp32 accumulate.
+
+    q, k, v: contiguous bfloat16 [B, H, T, D] on the GPU.  Returns ``out``.
+    """
+    return _tra("tra_fwd", torch.bfloat16, q, k, v, beta, p, out, stream)
+
+
+def tra_fwd_f32(q, k, v, beta, p, out=None, stream=None):
+    """Threshold Rectified Attention forward, fp32 in / fp32 out."""
+    return _tra("tra_fwd_f32", torch.float32, q, k, v, beta, p, out, stream)
+
+
+def nsa_sel_fwd(q, k, v, block_idx, block_size, out=None, lse=None, stream=None,
+                want_lse: bool = True):
+    """NSA selection-branch forward (bf16 in / out, fp32 lse).
+
+    q: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: int32 [B, Hkv, T, S].
+    Returns (out, lse) -- lse is None when ``want_lse`` is False and no buffer
+    is given (the library then skips writing it).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    _check(block_idx, "block_idx", torch.int32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError("k, v must be [B, Hkv, T, D] matching q")
+    if block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, Hkv, T):
+        raise ValueError("block_idx must be [B, Hkv, T, S]")
+    S = block_idx.shape[3]
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, Hq, T):
+            raise ValueError("lse must be [B, Hq, T]")
+    rc = load_library().nsa_sel_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    block_idx.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None,
+                                    B, Hq, Hkv, T, D, int(block_size), S,
+                                    _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("nsa_sel_fwd", rc)
+    return out, lse

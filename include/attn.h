@@ -1,0 +1,123 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused, tiled causal-attention forwards for
+ * AMD Instinct MI355X (gfx950), hand-written HIP.
+ *
+ * Common rules for every entry point
+ * ----------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to memory the caller owns and
+ *    keeps alive until the work on `stream` has finished.  The library never
+ *    allocates, frees, or keeps a pointer after returning.
+ *  - Tensors are dense and row-major (contiguous) in the shapes given below;
+ *    "bf16" means IEEE bfloat16 stored as 16-bit words.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued asynchronously; no call synchronises the device or the host.
+ *  - Output buffers are fully overwritten (every element is written).
+ *  - All arguments are validated on the host before any HIP call.  On a
+ *    validation error nothing is enqueued.  Element offsets are computed in
+ *    64-bit, so tensors may exceed 2^31 elements.
+ *  - The library is stateless and may be called from several host threads.
+ *  - A size of zero in B, H/Hq or T is a successful no-op.
+ *
+ * Return value: ATTN_OK (0) on success, otherwise one of the negative
+ * ATTN_ERR_* codes below; attn_status_str() names each.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_OK 0
+#define ATTN_ERR_NULL (-1)        /* a required pointer is NULL */
+#define ATTN_ERR_SHAPE (-2)       /* negative size, inconsistent shape, bad scalar */
+#define ATTN_ERR_UNSUPPORTED (-3) /* valid but not built: head dim, block size, group size */
+#define ATTN_ERR_ALIGN (-4)       /* a tensor pointer is not 16-byte aligned */
+#define ATTN_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
+
+/*
+ * Threshold Rectified Attention forward, bf16 in / bf16 out.
+ *
+ * Source: snap-research/TDA, page "triton_threshold_attention.py" -- module
+ * docstring (out = ReLU(Q K^T - tau)^p V, tau(i) = beta*sqrt(2 log(i+1)/d))
+ * and `_threshold_rela_fwd_kernel` (0-based query position i, natural log,
+ * d = head dim, only keys j <= i contribute, fp32 accumulation).
+ *
+ *   out[b,h,i,:] = sum_{j<=i} max(q_i . k_j - tau_i, 0)^p * v_j
+ *   tau_i        = beta * sqrt(2 * ln(i + 1) / D)
+ *
+ * There is no 1/sqrt(D) scale, no softmax and no normalisation.  A masked
+ * pair (j > i) contributes exactly 0 for every beta.
+ *
+ *   q, k, v : bf16 [B, H, T, D]      (read only)
+ *   out     : bf16 [B, H, T, D]      (written; may not alias q, k or v)
+ *   D       : 64 or 128 (else ATTN_ERR_UNSUPPORTED)
+ *   beta    : finite (else ATTN_ERR_SHAPE)
+ *   p       : finite and > 0 (else ATTN_ERR_SHAPE); p == 1 and p == 2 take
+ *             exact fast paths, any other p uses exp2(p * log2(x)).
+ *
+ * Numerics: q.k in bf16 x bf16 products with fp32 accumulation; the weight
+ * ReLU(.)^p is computed in fp32 and rounded to bf16 (nearest-even) before
+ * it multiplies V; the output accumulates in fp32 and is rounded to bf16.
+ */
+int tra_fwd(const void *q, const void *k, const void *v, void *out,
+            int B, int H, int T, int D, float beta, float p, void *stream);
+
+/*
+ * Threshold Rectified Attention forward, fp32 in / fp32 out.
+ * Same definition, arguments and errors as tra_fwd; every value (scores,
+ * weights, accumulation) is fp32.  Source: as for tra_fwd (the page's
+ * forward runs its kernel on fp32 copies of the inputs).
+ */
+int tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
+                int B, int H, int T, int D, float beta, float p, void *stream);
+
+/*
+ * NSA selection-branch forward, bf16 in / bf16 out, fp32 lse.
+ *
+ * Source: msb-msb/openbox-llm, page "nsa_selection_kernel.py" -- module
+ * docstring (GQA layout, Hq = Hkv * G, kv head of query head h is h / G, the
+ * S selected blocks per (batch, kv head, query) are shared by the G heads of
+ * the group, -1 slots are padding, causal j <= i, softmax with scale D^-0.5,
+ * a query with no valid block outputs 0), `selection_forward_reference`
+ * (the selection is a set: a block listed twice is attended once) and
+ * `_selection_fwd_kernel` (lse = max + log(sum) of the scaled scores, natural
+ * log, finite sentinel -1e9 for an empty row).
+ *
+ * For query i of head h (kv = h / G), A = the union over slots s of the
+ * tokens j of block blk = block_idx[b,kv,i,s] (blk*block_size <= j <
+ * (blk+1)*block_size) with j <= i.  A negative slot, or a block id >=
+ * T/block_size, adds nothing.  With s_j = (q_i . k_j) / sqrt(D):
+ *   out[b,h,i,:] = sum_{j in A} softmax_j(s) v_j,   lse[b,h,i] = ln sum_{j in A} exp(s_j)
+ * and an empty A gives out = 0 (exactly) and lse = -1e9 (exactly).
+ *
+ *   q          : bf16  [B, Hq, T, D]
+ *   k, v       : bf16  [B, Hkv, T, D]
+ *   block_idx  : int32 [B, Hkv, T, S]
+ *   out        : bf16  [B, Hq, T, D]  (written)
+ *   lse        : fp32  [B, Hq, T]     (written; may be NULL to skip it)
+ *   D          : 64 or 128                     (else ATTN_ERR_UNSUPPORTED)
+ *   block_size : 32, 64 or 128                 (else ATTN_ERR_UNSUPPORTED)
+ *   Hq % Hkv   : must be 0                     (else ATTN_ERR_SHAPE)
+ *   G = Hq/Hkv : 1 .. 16                       (else ATTN_ERR_UNSUPPORTED)
+ *   T          : a multiple of block_size      (else ATTN_ERR_SHAPE)
+ *   S          : >= 1                          (else ATTN_ERR_SHAPE)
+ *
+ * Numerics: scores in fp32 from bf16 products; softmax state (running max,
+ * sum, accumulator) in fp32; probabilities rounded to bf16 before they
+ * multiply V; out rounded to bf16.
+ */
+int nsa_sel_fwd(const void *q, const void *k, const void *v, const int32_t *block_idx,
+                void *out, float *lse,
+                int B, int Hq, int Hkv, int T, int D, int block_size, int S, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

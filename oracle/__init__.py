@@ -1,0 +1,167 @@
+"""fp64 CPU oracle for the two causal-attention forwards -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never calls it, and it
+shares no code with the HIP library: ``oracle.c`` is plain C compiled with gcc.
+
+Functions
+---------
+``tra_ref(q, k, v, beta, p, rows=None)``
+    Threshold Rectified Attention, out_i = sum_{j<=i} ReLU(q_i.k_j - tau_i)^p v_j,
+    tau_i = beta*sqrt(2 ln(i+1)/D).  Source: snap-research/TDA page
+    "triton_threshold_attention.py", module docstring and the forward kernel.
+``nsa_ref(q, k, v, block_idx, block_size, rows=None)``
+    NSA selection-branch forward (GQA softmax over the union of the selected
+    blocks' causal tokens, scale D^-0.5), returning (out, lse).  Source:
+    msb-msb/openbox-llm page "nsa_selection_kernel.py", module docstring,
+    ``selection_forward_reference`` and the lse definition in the query-outer
+    kernel.
+
+Inputs are CPU ``torch`` tensors (float32 or bfloat16) or numpy arrays
+(float32, or uint16 holding bf16 bits); they are read bit for bit and widened
+exactly to float64 inside the C code.  ``rows`` optionally restricts the work
+to a list of flat row ids ((b*H + h)*T + i); the result then has one row per
+id, in that order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_F32, _BF16 = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp64, OpenMP, no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    lib.oracle_tra_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                                    dbl, dbl, vp, i64, vp, ctypes.c_int]
+    lib.oracle_tra_rows.restype = ctypes.c_int
+    lib.oracle_nsa_rows.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64,
+                                    i64, i64, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_nsa_rows.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses by default (OMP_NUM_THREADS or cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _as_input(x):
+    """Return (contiguous numpy array, dtype code) holding x's exact bits."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16), _BF16
+            if x.dtype == torch.float32:
+                return x.numpy(), _F32
+            raise TypeError(f"oracle takes float32 or bfloat16, got {x.dtype}")
+    except ImportError:  # pragma: no cover - torch is always present here
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, _F32
+    if x.dtype == np.uint16:
+        return x, _BF16
+    raise TypeError(f"oracle takes float32 or bf16-bit uint16 arrays, got {x.dtype}")
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, None
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    return r, r.ctypes.data
+
+
+def tra_ref(q, k, v, beta: float, p: float, rows=None, nthreads: int = 0) -> np.ndarray:
+    """Threshold Rectified Attention forward in fp64.
+
+    q, k, v: [B, H, T, D].  Returns float64 [B, H, T, D], or [len(rows), D].
+    """
+    qa, dt = _as_input(q)
+    ka, dtk = _as_input(k)
+    va, dtv = _as_input(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share one dtype")
+    if not (qa.shape == ka.shape == va.shape) or qa.ndim != 4:
+        raise ValueError("q, k, v must all be [B, H, T, D]")
+    B, H, T, D = qa.shape
+    r, rp = _rows_arg(rows)
+    n = B * H * T if r is None else r.size
+    out = np.zeros((n, D), dtype=np.float64)
+    rc = _load().oracle_tra_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                                 B, H, T, D, float(beta), float(p), rp, n,
+                                 out.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_tra_rows rejected its arguments")
+    return out.reshape(B, H, T, D) if r is None else out
+
+
+def nsa_ref(q, k, v, block_idx, block_size: int, rows=None, nthreads: int = 0):
+    """NSA selection-branch forward in fp64.
+
+    q: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: [B, Hkv, T, S] ints.
+    Returns (out, lse): float64 [B, Hq, T, D] and [B, Hq, T] (or per-row).
+    """
+    qa, dt = _as_input(q)
+    ka, dtk = _as_input(k)
+    va, dtv = _as_input(v)
+    if not (dt == dtk == dtv):
+        raise TypeError("q, k, v must share one dtype")
+    try:
+        import torch
+        if isinstance(block_idx, torch.Tensor):
+            block_idx = block_idx.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    idx = np.ascontiguousarray(np.asarray(block_idx).astype(np.int32))
+    B, Hq, T, D = qa.shape
+    Hkv = ka.shape[1]
+    if ka.shape != (B, Hkv, T, D) or va.shape != ka.shape:
+        raise ValueError("k, v must be [B, Hkv, T, D] matching q")
+    if idx.ndim != 4 or idx.shape[:3] != (B, Hkv, T):
+        raise ValueError("block_idx must be [B, Hkv, T, S]")
+    S = idx.shape[3]
+    r, rp = _rows_arg(rows)
+    n = B * Hq * T if r is None else r.size
+    out = np.zeros((n, D), dtype=np.float64)
+    lse = np.zeros((n,), dtype=np.float64)
+    rc = _load().oracle_nsa_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, dt,
+                                 idx.ctypes.data, B, Hq, Hkv, T, D, int(block_size), S,
+                                 rp, n, out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_nsa_rows rejected its arguments")
+    if r is None:
+        return out.reshape(B, Hq, T, D), lse.reshape(B, Hq, T)
+    return out, lse

@@ -1,0 +1,216 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU implementation of the two causal-attention forwards
+ * that the HIP library computes.  It exists so that tests, the smoke check and
+ * the benchmark's CPU-baseline leg have something independent to compare the
+ * GPU against.  It shares no code, header, table or constant with the HIP
+ * library, and no product code path may call it.
+ *
+ * Inputs are the exact values handed to the GPU: either fp32 arrays or bf16
+ * bit patterns (uint16), widened exactly to double here.  Every sum, product,
+ * log, sqrt, pow and exp below is carried out in double precision in the
+ * order the definition states it (no tiling, no fusion, no reordering).
+ *
+ * Threshold Rectified Attention
+ *   source: snap-research/TDA, page "triton_threshold_attention.py",
+ *   module docstring (the formula out = ReLU(Q K^T - tau)^p V with
+ *   tau(i) = beta*sqrt(2*log(i+1)/d)) and `_threshold_rela_fwd_kernel`
+ *   (query position is 0-based, so the log takes position+1; natural log;
+ *   d is the head dimension; key j contributes only when j <= i).
+ *
+ * NSA selection branch
+ *   source: msb-msb/openbox-llm, page "nsa_selection_kernel.py", module
+ *   docstring (GQA layout, kv head = h // G, slots of -1 are padding, causal
+ *   j <= i, softmax, a query with no valid block outputs 0) and
+ *   `selection_forward_reference` (the selected blocks form a SET: a block
+ *   listed twice is attended once; scale = D^-0.5); `_selection_fwd_kernel`
+ *   (lse = max + log(sum) over the scaled scores, natural log, with the
+ *   finite sentinel -1e9 for an empty row).
+ *
+ * Threading: rows are independent; OpenMP spreads them over threads.  Each
+ * row is computed by exactly one thread in a fixed order, so results do not
+ * depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* dtype codes for the input arrays */
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Widen element `idx` of an fp32 or bf16 array to double (exact). */
+static double widen(const void *p, int dtype, int64_t idx) {
+    if (dtype == ORACLE_F32) return (double)((const float *)p)[idx];
+    uint32_t bits = (uint32_t)((const uint16_t *)p)[idx] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Threshold Rectified Attention forward for a list of output rows.
+ *
+ *   q, k, v : [B, H, T, D] dense row-major, fp32 or bf16 bits (dtype)
+ *   rows    : flat row ids r = (b*H + h)*T + i, or NULL for all B*H*T rows
+ *   out     : [nrows, D] doubles, row n holds out[rows[n], :]
+ *
+ *   out[b,h,i,:] = sum_{j=0..i} max(q_i . k_j - tau_i, 0)^p * v_j
+ *   tau_i        = beta * sqrt(2 * ln(i + 1) / D)
+ *
+ * No 1/sqrt(D) scale, no softmax, no normalisation.  x^p is libm pow(); a
+ * non-positive x contributes nothing (ReLU).  Returns 0, or -1 on bad args.
+ */
+int oracle_tra_rows(const void *q, const void *k, const void *v, int dtype,
+                    int64_t B, int64_t H, int64_t T, int64_t D,
+                    double beta, double p,
+                    const int64_t *rows, int64_t nrows,
+                    double *out, int nthreads) {
+    if (!q || !k || !v || !out || B < 0 || H < 0 || T < 0 || D <= 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t total = B * H * T;
+    if (!rows) nrows = total;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t n = 0; n < nrows; ++n) {
+        const int64_t r = rows ? rows[n] : n;
+        double *o = out + n * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (r < 0 || r >= total) { bad = 1; continue; }
+        const int64_t bh = r / T, i = r % T;
+        const int64_t head = bh * T * D;           /* start of this (b,h) slab */
+        const double tau = beta * sqrt(2.0 * log((double)(i + 1)) / (double)D);
+        for (int64_t j = 0; j <= i; ++j) {
+            double s = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                s += widen(q, dtype, head + i * D + d) * widen(k, dtype, head + j * D + d);
+            const double x = s - tau;
+            if (!(x > 0.0)) continue;
+            const double w = pow(x, p);
+            for (int64_t d = 0; d < D; ++d)
+                o[d] += w * widen(v, dtype, head + j * D + d);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * NSA selection-branch forward for a list of output rows.
+ *
+ *   q         : [B, Hq, T, D]   fp32 or bf16 bits (dtype)
+ *   k, v      : [B, Hkv, T, D]
+ *   block_idx : [B, Hkv, T, S]  int32; any negative value is padding
+ *   rows      : flat row ids r = (b*Hq + h)*T + i, or NULL for all rows
+ *   out       : [nrows, D] doubles;  lse : [nrows] doubles (may be NULL)
+ *
+ * For query i of head h (group G = Hq/Hkv, kv head = h / G) the attended set
+ * A is the union over slots of the tokens of block blk = block_idx[b,kv,i,s]
+ * (tokens blk*bs .. blk*bs+bs-1) that satisfy j <= i.  A slot that is
+ * negative or names a block at or past T/bs adds nothing; a block listed in
+ * several slots is counted once.  Then, with scale = 1/sqrt(D),
+ *
+ *   s_j  = scale * (q_i . k_j)             for j in A
+ *   out  = sum_j exp(s_j - M) v_j / sum_j exp(s_j - M),  M = max_j s_j
+ *   lse  = M + ln(sum_j exp(s_j - M))      (= ln sum_j exp(s_j))
+ *
+ * and an empty A gives out = 0, lse = -1e9.  Keys are visited in increasing
+ * position order.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_nsa_rows(const void *q, const void *k, const void *v, int dtype,
+                    const int32_t *block_idx,
+                    int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                    int64_t bs, int64_t S,
+                    const int64_t *rows, int64_t nrows,
+                    double *out, double *lse, int nthreads) {
+    if (!q || !k || !v || !block_idx || !out) return -1;
+    if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || D <= 0 || bs <= 0 || S < 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t G = Hq / Hkv;
+    const int64_t nblk = T / bs;
+    const int64_t total = B * Hq * T;
+    const double scale = 1.0 / sqrt((double)D);
+    if (!rows) nrows = total;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        unsigned char *chosen = (unsigned char *)calloc((size_t)(nblk > 0 ? nblk : 1), 1);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+        if (!chosen || !sc) bad = 1;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t n = 0; n < nrows; ++n) {
+            if (!chosen || !sc) continue;
+            const int64_t r = rows ? rows[n] : n;
+            double *o = out + n * D;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            if (lse) lse[n] = -1e9;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            const int64_t bh = r / T, i = r % T;
+            const int64_t b = bh / Hq, h = bh % Hq;
+            const int64_t kvh = h / G;
+            const int64_t qrow = (bh * T + i) * D;
+            const int64_t kvslab = (b * Hkv + kvh) * T * D;
+            const int32_t *slots = block_idx + ((b * Hkv + kvh) * T + i) * S;
+
+            /* the set of selected blocks */
+            memset(chosen, 0, (size_t)(nblk > 0 ? nblk : 1));
+            for (int64_t s = 0; s < S; ++s) {
+                const int64_t blk = slots[s];
+                if (blk >= 0 && blk < nblk) chosen[blk] = 1;
+            }
+            /* scores over the attended tokens, increasing position */
+            int64_t na = 0;
+            double M = -INFINITY;
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                if (!chosen[blk]) continue;
+                for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d)
+                        dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
+                    const double s = scale * dot;
+                    sc[j] = s;
+                    if (s > M) M = s;
+                    ++na;
+                }
+            }
+            if (na == 0) continue;                 /* empty row: 0 and -1e9 */
+            double l = 0.0;
+            for (int64_t blk = 0; blk < nblk; ++blk) {
+                if (!chosen[blk]) continue;
+                for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
+                    const double e = exp(sc[j] - M);
+                    l += e;
+                    for (int64_t d = 0; d < D; ++d) o[d] += e * widen(v, dtype, kvslab + j * D + d);
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) o[d] /= l;
+            if (lse) lse[n] = M + log(l);
+        }
+        free(chosen);
+        free(sc);
+    }
+    return bad ? -1 : 0;
+}
