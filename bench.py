@@ -1,0 +1,226 @@
+"""Benchmark of the fused causal-attention forwards on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass over both forwards of the hot path, each on its own
+seeded synthetic batch already resident in HBM:
+  * tra_fwd      Threshold Rectified Attention, bf16, B=2 H=32 T=8192 D=128,
+                 beta=1, p=2 (useful FLOPs = 4*D per causal pair j <= i);
+  * nsa_sel_fwd  NSA selection branch, bf16, B=1 Hq=64 Hkv=4 T=32768 D=128,
+                 block_size=64, S=16 (gathered bytes = 2*block_size*D*2 per
+                 valid selected block per (b, kv head, query)).
+W untimed steps, then K timed steps between two device synchronisations.
+Per-launch kernel durations come from HIP events recorded on the stream the
+kernels run on.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import causal_attention_tiled_amd as cat  # noqa: E402
+from causal_attention_tiled_amd import inputs  # noqa: E402
+
+METRIC = ("useful causal-attn fwd TFLOP/s + % bf16 MFMA peak (T=8K,D=128); NSA fwd GB/s")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+
+TRA = dict(B=2, H=32, T=8192, D=128, beta=1.0, p=2.0)
+NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
+
+
+def tra_useful_flops(B, H, T, D, rows=None):
+    """4*D flops (q.k and w*v) per causal pair; rows = flat ids, else all rows."""
+    if rows is None:
+        return 4.0 * D * B * H * T * (T + 1) / 2.0
+    i = np.asarray(rows) % T
+    return float(4.0 * D * np.sum(i + 1))
+
+
+def nsa_gathered_bytes(idx, T, bs, D, rows_kv=None):
+    """2 (K and V) * bs * D * 2 bytes per valid, distinct, causally reachable
+    selected block per (b, kv head, query).  rows_kv: flat (b*Hkv+kv)*T+i ids."""
+    nblk = T // bs
+    flat = idx.reshape(-1, idx.shape[-1])
+    if rows_kv is not None:
+        flat = flat[np.asarray(rows_kv)]
+        pos = np.asarray(rows_kv) % T
+    else:
+        pos = np.arange(flat.shape[0]) % T
+    valid = (flat >= 0) & (flat < nblk) & (flat * bs <= pos[:, None])
+    # distinct blocks only
+    srt = np.sort(np.where(valid, flat, -1), axis=1)
+    distinct = (srt >= 0) & np.concatenate([np.ones((srt.shape[0], 1), bool),
+                                            srt[:, 1:] != srt[:, :-1]], axis=1)
+    return float(distinct.sum()) * 2 * bs * D * 2
+
+
+def cpu_baseline(q, k, v, idx_np, budget_s=12.0):
+    """Time the fp64 oracle on bounded samples of both workloads."""
+    import oracle
+    threads = oracle.num_threads()
+    rng = np.random.default_rng(123)
+    B, H, T, D = TRA["B"], TRA["H"], TRA["T"], TRA["D"]
+    # TRA: rows drawn uniformly, growing the sample until about budget_s/2 elapses
+    n, spent, flops, nrows = 8, 0.0, 0.0, 0
+    while spent < budget_s / 2 and n <= 1 << 16:
+        rows = rng.integers(0, B * H * T, size=n)
+        t0 = time.perf_counter()
+        oracle.tra_ref(q, k, v, TRA["beta"], TRA["p"], rows=rows)
+        spent += time.perf_counter() - t0
+        flops += tra_useful_flops(B, H, T, D, rows)
+        nrows += n
+        n *= 2
+    tra_tflops = flops / spent / 1e12
+    return {"value": tra_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nrows} uniformly drawn rows of tra_fwd B=2 H=32 T=8192 D=128 p=2 "
+                      f"({flops:.3g} useful FLOPs in {spent:.1f} s), fp64"}
+
+
+def cpu_baseline_nsa(qn, kn, vn, idx_np, budget_s=8.0):
+    import oracle
+    rng = np.random.default_rng(321)
+    B, Hq, Hkv, T, D, bs = NSA["B"], NSA["Hq"], NSA["Hkv"], NSA["T"], NSA["D"], NSA["block_size"]
+    G = Hq // Hkv
+    n, spent, nbytes, nrows = 64, 0.0, 0.0, 0
+    while spent < budget_s and n <= 1 << 18:
+        rows = rng.integers(0, B * Hq * T, size=n)
+        t0 = time.perf_counter()
+        oracle.nsa_ref(qn, kn, vn, idx_np, bs, rows=rows)
+        spent += time.perf_counter() - t0
+        bh = rows // T
+        kv_rows = ((bh // Hq) * Hkv + (bh % Hq) // G) * T + rows % T
+        nbytes += nsa_gathered_bytes(idx_np, T, bs, D, kv_rows) / G   # one head of G
+        nrows += n
+        n *= 2
+    return {"value": nbytes / spent / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{nrows} uniformly drawn (head, query) rows of nsa_sel_fwd T=32768 G=16 "
+                      f"({spent:.1f} s), fp64; bytes counted per head"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["tra", "nsa"], default=None,
+                    help="launch only one of the two forwards (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forwards are single-GPU kernels; sharding is described, not run)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    cat.load_library()
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = inputs.tra_inputs(TRA["B"], TRA["H"], TRA["T"], TRA["D"], seed=0)
+    qn, kn, vn = inputs.nsa_inputs(NSA["B"], NSA["Hq"], NSA["Hkv"], NSA["T"], NSA["D"], seed=0)
+    idx_np = inputs.nsa_block_idx(NSA["B"], NSA["Hkv"], NSA["T"], NSA["block_size"], NSA["S"],
+                                  seed=0)
+    gq, gk, gv = q.to(dev), k.to(dev), v.to(dev)
+    gqn, gkn, gvn = qn.to(dev), kn.to(dev), vn.to(dev)
+    gidx = torch.from_numpy(idx_np).to(dev)
+    out = torch.empty_like(gq)
+    o_n = torch.empty_like(gqn)
+    lse_n = torch.empty(NSA["B"], NSA["Hq"], NSA["T"], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    run_tra = args.only in (None, "tra")
+    run_nsa = args.only in (None, "nsa")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        if run_tra:
+            cat.tra_fwd(gq, gk, gv, TRA["beta"], TRA["p"], out=out)
+        if ev is not None:
+            ev[1].record()
+        if run_nsa:
+            cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n)
+        if ev is not None:
+            ev[2].record()
+
+    print("bench: warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    tra_ms = [e[0].elapsed_time(e[1]) for e in events]
+    nsa_ms = [e[1].elapsed_time(e[2]) for e in events]
+    tra_avg = float(np.mean(tra_ms)) if run_tra else 0.0
+    nsa_avg = float(np.mean(nsa_ms)) if run_nsa else 0.0
+
+    flops = tra_useful_flops(TRA["B"], TRA["H"], TRA["T"], TRA["D"])
+    gbytes = nsa_gathered_bytes(idx_np, NSA["T"], NSA["block_size"], NSA["D"])
+    tra_tflops = flops / (tra_avg * 1e-3) / 1e12 if run_tra else 0.0
+    nsa_gbps = gbytes / (nsa_avg * 1e-3) / 1e9 if run_nsa else 0.0
+
+    roof_tra = {"kernel": "tra_fwd_bf16_kernel<128,p=2>", "bound": "mfma",
+                "achieved": tra_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tra_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch": f"{flops:.6g} useful FLOPs / {tra_avg:.4f} ms avg launch"}
+    roof_nsa = {"kernel": "nsa_sel_fwd_kernel<128,64>", "bound": "hbm",
+                "achieved": nsa_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": nsa_gbps / PEAK_HBM_GBPS, "traffic": None,
+                "per_launch": f"{gbytes:.6g} gathered K/V bytes / {nsa_avg:.4f} ms avg launch"}
+    dominant = roof_nsa if nsa_avg >= tra_avg else roof_tra
+
+    result = {
+        "metric": METRIC,
+        "value": tra_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0, D^-1/2) q,k and N(0,1) v for tra_fwd; N(0,1) q,k,v and "
+                "seeded random block lists (own block + 15 distinct earlier) for nsa_sel_fwd",
+        "config": {"workload": "tra_fwd B2 H32 T8192 D128 beta1 p2 + nsa_sel_fwd B1 Hq64 Hkv4 "
+                               "T32768 D128 bs64 S16",
+                   "tra": TRA, "nsa": NSA},
+        "tra_fwd": {"ms": tra_avg, "tflops": tra_tflops,
+                    "frac_bf16_peak": tra_tflops / PEAK_BF16_TFLOPS},
+        "nsa_sel_fwd": {"ms": nsa_avg, "gathered_gb": gbytes / 1e9, "gbps": nsa_gbps,
+                        "frac_hbm_peak": nsa_gbps / PEAK_HBM_GBPS},
+        "roofline": dominant,
+        "roofline_all": {"tra_fwd": roof_tra, "nsa_sel_fwd": roof_nsa},
+    }
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, idx_np)
+        result["cpu_baseline_nsa"] = cpu_baseline_nsa(qn, kn, vn, idx_np)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

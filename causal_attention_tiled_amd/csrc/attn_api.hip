@@ -1,0 +1,94 @@
+// attn_api.hip -- the C ABI of libattn.so (declared in include/attn.h).
+//
+// Every argument is validated on the host before any HIP call; then the kernel is
+// launched asynchronously on the caller's stream.  Nothing is allocated, nothing is
+// synchronised, no state is kept between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_internal.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// The grid is one dimension of at most 2^31-1 workgroups.
+bool grid_fits(int64_t n) { return n > 0 && n <= 0x7fffffffLL; }
+
+int tra_validate(const void *q, const void *k, const void *v, const void *out, int B, int H,
+                 int T, int D, float beta, float p, int rows_per_wg, bool *noop) {
+    *noop = false;
+    if (B < 0 || H < 0 || T < 0 || D < 0) return ATTN_ERR_SHAPE;
+    if (!isfinite(beta) || !isfinite(p) || !(p > 0.0f)) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || T == 0) {
+        *noop = true;
+        return ATTN_OK;
+    }
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
+    if (!grid_fits((int64_t)B * H * ((T + rows_per_wg - 1) / rows_per_wg))) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, int B, int H,
+                        int T, int D, float beta, float p, void *stream) {
+    bool noop;
+    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, 128, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const hipError_t e = attn::launch_tra_fwd_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out), B * H, T, D, beta, p,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT int tra_fwd_f32(const float *q, const float *k, const float *v, float *out, int B,
+                            int H, int T, int D, float beta, float p, void *stream) {
+    bool noop;
+    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, 64, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const hipError_t e = attn::launch_tra_fwd_f32(q, k, v, out, B * H, T, D, beta, p,
+                                                  static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
+                            const int32_t *block_idx, void *out, float *lse, int B, int Hq,
+                            int Hkv, int T, int D, int block_size, int S, void *stream) {
+    if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || D < 0 || S < 1 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != 32 && block_size != 64 && block_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+    if (T % block_size != 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || Hq == 0 || T == 0) return ATTN_OK;
+    if (!q || !k || !v || !block_idx || !out) return ATTN_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_idx) & 3u) != 0) return ATTN_ERR_ALIGN;
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
+    if (!grid_fits((int64_t)B * Hkv * ((T + 3) / 4))) return ATTN_ERR_SHAPE;
+    const hipError_t e = attn::launch_nsa_sel_fwd(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), block_idx, static_cast<uint16_t *>(out), lse, B, Hq,
+        Hkv, T, D, block_size, S, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_EXPORT const char *attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "null pointer argument";
+        case ATTN_ERR_SHAPE: return "invalid shape or scalar argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, block size or group size";
+        case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+        case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,59 @@
+// attn_internal.h -- types and helpers shared by the gfx950 kernels of libattn.so.
+// Internal to the library; the public C ABI is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lanes: A[m = lane%32][k = 8*(lane/32)+t],
+// B[k = 8*(lane/32)+t][n = lane%32], t = 0..7.  Accumulator: C[m][n] with n = lane%32,
+// m = 8*(r/4) + 4*(lane/32) + r%4 for register r = 0..15.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Operand lanes: A[m = lane%16][k = 8*(lane/16)+t],
+// B[k = 8*(lane/16)+t][n = lane%16].  Accumulator: C[m][n] with n = lane%16,
+// m = 4*(lane/16) + r for register r = 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Order LDS traffic between the lanes of one wavefront (a write by one lane
+// that another lane of the same wave reads next).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Host-side launchers (one per kernel family); they pick the template
+// instance and return the HIP launch status.
+hipError_t launch_tra_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               uint16_t *out, int BH, int T, int D, float beta, float p,
+                               hipStream_t stream);
+hipError_t launch_tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
+                              int BH, int T, int D, float beta, float p, hipStream_t stream);
+hipError_t launch_nsa_sel_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *block_idx, uint16_t *out, float *lse, int B,
+                              int Hq, int Hkv, int T, int D, int block_size, int S,
+                              hipStream_t stream);
+
+}  // namespace attn

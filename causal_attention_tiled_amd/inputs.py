@@ -64,9 +64,10 @@ def nsa_block_idx(B: int, Hkv: int, T: int, block_size: int, S: int, seed: int =
             c = own[r0:r1]                                   # candidates are 0 .. c-1
             keys = rng.random((r1 - r0, nblk))
             keys[cols[None, :] >= c[:, None]] = 2.0          # not a candidate
-            order = np.argsort(keys, axis=1, kind="stable")[:, :extra]
-            take = np.arange(extra)[None, :] < np.minimum(c, extra)[:, None]
-            out[r0:r1, 1:] = np.where(take, order, -1).astype(np.int32)
+            width = min(extra, nblk)
+            order = np.argsort(keys, axis=1, kind="stable")[:, :width]
+            take = np.arange(width)[None, :] < np.minimum(c, width)[:, None]
+            out[r0:r1, 1:1 + width] = np.where(take, order, -1).astype(np.int32)
     return out.reshape(B, Hkv, T, S)
 
 

@@ -16,7 +16,8 @@
  *    validation error nothing is enqueued.  Element offsets are computed in
  *    64-bit, so tensors may exceed 2^31 elements.
  *  - The library is stateless and may be called from several host threads.
- *  - A size of zero in B, H/Hq or T is a successful no-op.
+ *  - A size of zero in B, H/Hq or T is a successful no-op once the other
+ *    arguments have been validated; the tensor pointers may then be NULL.
  *
  * Return value: ATTN_OK (0) on success, otherwise one of the negative
  * ATTN_ERR_* codes below; attn_status_str() names each.

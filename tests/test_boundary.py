@@ -1,0 +1,112 @@
+"""The C ABI: libattn.so loads, exports every function include/attn.h declares,
+and rejects bad arguments on the host before any HIP call (so these run on the
+CPU: the dummy pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN = 0, -1, -2, -3, -4
+P = 0x10000  # a 16-byte aligned dummy address (never touched by validation)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import causal_attention_tiled_amd as cat
+    if not os.path.exists(cat.library_path()):
+        from causal_attention_tiled_amd import build
+        build.build()
+    return cat.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tra_fwd", "tra_fwd_f32", "nsa_sel_fwd", "attn_status_str"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} is declared in attn.h but not exported"
+
+
+def test_status_strings(lib):
+    import causal_attention_tiled_amd as cat
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, -5):
+        assert cat.attn_status_str(code) not in ("", "unknown status")
+    assert cat.attn_status_str(12345) == "unknown status"
+
+
+def _tra(lib, fn, q=P, k=P, v=P, o=P, B=1, H=1, T=8, D=128, beta=1.0, p=2.0):
+    return getattr(lib, fn)(q, k, v, o, B, H, T, D, beta, p, None)
+
+
+@pytest.mark.parametrize("fn", ["tra_fwd", "tra_fwd_f32"])
+def test_tra_validation(lib, fn):
+    assert _tra(lib, fn, q=None) == ENULL
+    assert _tra(lib, fn, o=None) == ENULL
+    assert _tra(lib, fn, T=-1) == ESHAPE
+    assert _tra(lib, fn, B=-2) == ESHAPE
+    assert _tra(lib, fn, p=0.0) == ESHAPE
+    assert _tra(lib, fn, p=-1.0) == ESHAPE
+    assert _tra(lib, fn, p=float("nan")) == ESHAPE
+    assert _tra(lib, fn, beta=float("inf")) == ESHAPE
+    assert _tra(lib, fn, D=96) == EUNSUP
+    assert _tra(lib, fn, D=256) == EUNSUP
+    assert _tra(lib, fn, k=P + 8) == EALIGN
+    assert _tra(lib, fn, o=P + 2) == EALIGN
+    # empty problems are no-ops, even with NULL tensors
+    assert _tra(lib, fn, q=None, k=None, v=None, o=None, B=0) == OK
+    assert _tra(lib, fn, q=None, k=None, v=None, o=None, T=0) == OK
+    # ...but the other arguments are still checked
+    assert _tra(lib, fn, T=0, D=96) == EUNSUP
+
+
+def _nsa(lib, q=P, k=P, v=P, idx=P, o=P, lse=P, B=1, Hq=8, Hkv=2, T=128, D=128, bs=64, S=4):
+    return lib.nsa_sel_fwd(q, k, v, idx, o, lse, B, Hq, Hkv, T, D, bs, S, None)
+
+
+def test_nsa_validation(lib):
+    assert _nsa(lib, idx=None) == ENULL
+    assert _nsa(lib, q=None) == ENULL
+    assert _nsa(lib, Hq=6, Hkv=4) == ESHAPE          # Hq % Hkv
+    assert _nsa(lib, Hkv=0) == ESHAPE
+    assert _nsa(lib, T=100) == ESHAPE                # T % block_size
+    assert _nsa(lib, S=0) == ESHAPE
+    assert _nsa(lib, bs=16) == EUNSUP
+    assert _nsa(lib, bs=48) == EUNSUP
+    assert _nsa(lib, D=32) == EUNSUP
+    assert _nsa(lib, Hq=34, Hkv=2) == EUNSUP         # G = 17
+    assert _nsa(lib, v=P + 4) == EALIGN
+    assert _nsa(lib, idx=P + 2) == EALIGN
+    assert _nsa(lib, lse=P + 1) == EALIGN
+    assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, T=0) == OK
+    assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, B=0) == OK
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import causal_attention_tiled_amd as cat
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cat.tra_fwd(x, x, x, 1.0, 2.0)
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """Nothing in the package imports the oracle or computes on the CPU."""
+    pkg = os.path.join(ROOT, "causal_attention_tiled_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), name
+            assert "liboracle" not in src, name

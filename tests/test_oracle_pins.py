@@ -426,3 +426,14 @@ def test_block_idx_recipe():
         picks = rest[:n]
         assert len(set(picks.tolist())) == n and np.all((picks >= 0) & (picks < c))
     assert np.array_equal(idx, inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0))
+
+
+def test_block_idx_recipe_more_slots_than_blocks():
+    """S - 1 larger than the number of earlier blocks: every earlier block once."""
+    idx = inputs.nsa_block_idx(1, 1, 320, 32, 16, seed=1)
+    for i in range(320):
+        c = i // 32
+        row = idx[0, 0, i]
+        assert row[0] == c
+        assert sorted(row[1:1 + c].tolist()) == list(range(c))
+        assert np.all(row[1 + c:] == -1)
