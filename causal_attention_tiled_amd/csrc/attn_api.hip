@@ -39,7 +39,7 @@ int tra_validate(const void *q, const void *k, const void *v, const void *out, i
 ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, int B, int H,
                         int T, int D, float beta, float p, void *stream) {
     bool noop;
-    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, 128, &noop);
+    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, attn::kTraBf16Rows, &noop);
     if (st != ATTN_OK || noop) return st;
     const hipError_t e = attn::launch_tra_fwd_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
@@ -51,7 +51,7 @@ ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, 
 ATTN_EXPORT int tra_fwd_f32(const float *q, const float *k, const float *v, float *out, int B,
                             int H, int T, int D, float beta, float p, void *stream) {
     bool noop;
-    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, 64, &noop);
+    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, attn::kTraF32Rows, &noop);
     if (st != ATTN_OK || noop) return st;
     const hipError_t e = attn::launch_tra_fwd_f32(q, k, v, out, B * H, T, D, beta, p,
                                                   static_cast<hipStream_t>(stream));

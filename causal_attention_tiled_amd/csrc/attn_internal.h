@@ -44,6 +44,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Query rows per workgroup of the bf16 / fp32 Threshold Rectified Attention kernels.
+constexpr int kTraBf16Rows = 256;
+constexpr int kTraF32Rows = 64;
+
 // Host-side launchers (one per kernel family); they pick the template
 // instance and return the HIP launch status.
 hipError_t launch_tra_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,

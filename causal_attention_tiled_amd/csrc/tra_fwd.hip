@@ -30,7 +30,8 @@ namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128;  // query rows per workgroup
+constexpr int kQueryBlocks = 2;  // 32-row query blocks per wave (64 rows per wave)
+static_assert(4 * 32 * kQueryBlocks == kTraBf16Rows, "workgroup rows");
 constexpr int kBN = 64;   // keys per LDS tile
 
 enum PowMode { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2 };
@@ -62,36 +63,43 @@ __device__ __forceinline__ void tra_tile_of(int bid, int BH, int nqt, int &bh, i
     }
 }
 
-// V^T tile in LDS: row = head dim d (D rows), column = key position in the tile.
-// Within each 16-key group the key offset o = 8a + 4b + c is stored at 8b + 4a + c
-// (bits 2 and 3 swapped) so that a lane's 8 MFMA k-values are 16 contiguous bytes.
-// The 4-key units of a row are XOR-swizzled by an even amount that depends on the
-// row, which spreads the transposing writes over the banks and keeps 8-key reads
-// contiguous.
-__device__ __forceinline__ int vt_pos_of_key(int o) {
-    return (o & ~15) | ((o & 4) << 1) | ((o & 8) >> 1) | (o & 3);
-}
-__device__ __forceinline__ int vt_offset(int row, int pos, int stride) {
-    const int unit = (pos >> 2) ^ ((row >> 2) & 14);  // even XOR < 16 units per row
-    return row * stride + (unit << 2) + (pos & 3);
+// LDS tile layout (K and V alike): row-major [key][dim], D*2 bytes per row, no
+// padding; the 16-byte chunk c of row r sits in chunk slot c ^ tile_swz(r).  With
+// this swizzle the 8 rows read by 8 consecutive lanes (K operand, ds_read_b128) and
+// the 4 rows x 32 bytes read by a 16-lane group (V operand, ds_read_b64_tr_b16) each
+// cover all banks once.
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource over `bytes` bytes at `base`; loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
-template <int D, int PM>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+template <int D, int PM, int QB>
 __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, int BH, int T, int nqt,
     float beta, float p) {
-    constexpr int KSTR = D + 8;    // K row stride in LDS (elements): 16 B of padding
-    constexpr int VSTR = kBN + 8;  // V^T row stride in LDS (elements)
-    constexpr int DC = D / 8;      // 16-byte chunks per head-dim row
-    constexpr int KLOADS = kBN * DC / kThreads;
-    constexpr int VBLK = (kBN / 4) * DC;  // 4-key x 8-dim blocks per tile
-    constexpr int NDS = D / 16;           // MFMA k-steps for S^T
-    constexpr int NDT = D / 32;           // 32-dim output tiles
-    static_assert(VBLK <= kThreads, "one V block per thread");
+    constexpr int BM = 4 * 32 * QB;             // query rows per workgroup
+    constexpr int ROWB = D * 2;                 // bytes per key row
+    constexpr int CH = D / 8;                   // 16-byte chunks per row
+    constexpr int TILEB = kBN * ROWB;           // bytes of one K (or V) tile
+    constexpr int LOADS = kBN * CH / kThreads;  // 16-byte chunks per thread per tensor
+    constexpr int NDS = D / 16;                 // S^T MFMA k-steps
+    constexpr int NDT = D / 32;                 // 32-dim output tiles
+    static_assert(LOADS >= 1 && kBN * CH % kThreads == 0, "tile staging");
+    static_assert(TILEB == 4 * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILEB];  // [buffer][K, V]
 
     int bh, qt;
     tra_tile_of(blockIdx.x, BH, nqt, bh, qt);
@@ -100,145 +108,203 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const size_t slab = (size_t)bh * T * D;
-    const uint16_t *Kg = K + slab;
-    const uint16_t *Vg = V + slab;
 
-    const int q0 = qt * kBM;
-    const int qw0 = q0 + wave * 32;
-    const int my_q = qw0 + l32;
-    const bool wave_active = qw0 < T;
-    const int wave_last = min(qw0 + 31, T - 1);
-    const int q_last = min(q0 + kBM, T) - 1;
+    // this wave's rows: qw0 + 32*qb + l32, qb < QB
+    const int q0 = qt * BM;
+    const int qw0 = q0 + wave * 32 * QB;
+    const int q_last = min(q0 + BM, T) - 1;
     const int ntiles = q_last / kBN + 1;
 
-    // Q^T operand: this lane's query, dims 16*ds + 8*hi .. +7.
-    bf16x8 qf[NDS];
-    {
-        const u32x4 z = {0u, 0u, 0u, 0u};
+    // Q^T operands and thresholds
+    bf16x8 qf[QB][NDS];
+    float tau[QB];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int myq = qw0 + 32 * qb + l32;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-            u32x4 r = z;
-            if (my_q < T) r = *(const u32x4 *)(Q + slab + (size_t)my_q * D + ds * 16 + hi * 8);
-            qf[ds] = as_bf16x8(r);
+            u32x4 r = zero4;
+            if (myq < T) r = *(const u32x4 *)(Q + slab + (size_t)myq * D + ds * 16 + hi * 8);
+            qf[qb][ds] = as_bf16x8(r);
         }
+        tau[qb] = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
     }
-    const float tau = beta * sqrtf(2.0f * logf((float)(my_q + 1)) / (float)D);
 
-    f32x16 oacc[NDT];
+    // S^T accumulators start from -tau of the lane's row, so the epilogue never
+    // subtracts the threshold.
+    f32x16 cinit[QB];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
-
-    u32x4 kr[KLOADS];
-    u32x4 vr[4];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    auto gload = [&](int n) {
-        const int k0 = n * kBN;
+        for (int r = 0; r < 16; ++r) cinit[qb][r] = -tau[qb];
+    // Causal mask of one 32-key block starting at kbase (only for blocks that reach
+    // past this wave's first row): register r holds key kbase + 8*(r/4) + 4*hi + r%4.
+    auto mask_block = [&](f32x16 (&sv)[QB], int kbase) {
 #pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int c = tid + r * kThreads;
-            const int key = k0 + c / DC;
-            kr[r] = key < T ? *(const u32x4 *)(Kg + (size_t)key * D + (c % DC) * 8) : zero4;
-        }
-        if (tid < VBLK) {
-            const int kg = tid / DC, dc = tid % DC;
+        for (int qb = 0; qb < QB; ++qb) {
+            const int lim = qw0 + 32 * qb + l32 - kbase - 4 * hi;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kg * 4 + r;
-                vr[r] = key < T ? *(const u32x4 *)(Vg + (size_t)key * D + dc * 8) : zero4;
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < KLOADS; ++r) {
-            const int c = tid + r * kThreads;
-            *(u32x4 *)(&Ks[buf][(c / DC) * KSTR + (c % DC) * 8]) = kr[r];
-        }
-        if (tid < VBLK) {
-            const int kg = tid / DC, dc = tid % DC;
-            const int pos = vt_pos_of_key(kg * 4);
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const int w = d >> 1;
-                uint32_t lo, hi2;
-                if (d & 1) {
-                    lo = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-                    hi2 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-                } else {
-                    lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-                    hi2 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-                }
-                const u32x2 pr = {lo, hi2};
-                *(u32x2 *)(&Vs[buf][vt_offset(dc * 8 + d, pos, VSTR)]) = pr;
-            }
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) > lim) sv[qb][r] = -INFINITY;
         }
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int n = 0; n < ntiles; ++n) {
-        const int buf = n & 1;
-        if (n + 1 < ntiles) gload(n + 1);
-        if (wave_active) {
+    f32x16 oacc[QB][NDT];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int kbase = n * kBN + kb * 32;
-                if (kbase <= wave_last) {
-                    f32x16 s;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
-#pragma unroll
-                    for (int ds = 0; ds < NDS; ++ds) {
-                        const bf16x8 a = *(const bf16x8 *)(&Ks[buf][(kb * 32 + l32) * KSTR +
-                                                                   ds * 16 + hi * 8]);
-                        s = mfma_32x32x16(a, qf[ds], s);
-                    }
-                    // epilogue: S^T register r holds key kbase + 8*(r/4) + 4*hi + r%4
-                    const bool diag = kbase + 31 > qw0;
-                    bf16x8 pf[2];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float w = relu_pow<PM>(s[r] - tau, p);
-                        if (diag) {
-                            const int key = kbase + 8 * (r >> 2) + 4 * hi + (r & 3);
-                            if (key > my_q) w = 0.0f;
-                        }
-                        pf[r >> 3][r & 7] = (__bf16)w;
-                    }
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const int row = dt * 32 + l32;
-#pragma unroll
-                        for (int c = 0; c < 2; ++c) {
-                            const int pos = kb * 32 + c * 16 + hi * 8;
-                            const bf16x8 a =
-                                *(const bf16x8 *)(&Vs[buf][vt_offset(row, pos, VSTR)]);
-                            oacc[dt] = mfma_32x32x16(a, pf[c], oacc[dt]);
-                        }
-                    }
-                }
-            }
-        }
-        if (n + 1 < ntiles) sstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // O^T accumulator: lane holds query my_q, dims 32*dt + 8*i + 4*hi + j.
-    if (my_q < T) {
-        uint16_t *orow = O + slab + (size_t)my_q * D;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x2 pr = {pack_bf16x2(oacc[dt][4 * i], oacc[dt][4 * i + 1]),
-                                  pack_bf16x2(oacc[dt][4 * i + 2], oacc[dt][4 * i + 3])};
-                *(u32x2 *)(orow + dt * 32 + 8 * i + 4 * hi) = pr;
-            }
+            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.0f;
+
+    // Staging: K and V tiles go from HBM straight into LDS (buffer_load ... lds).
+    // Instruction j of wave w fills LDS bytes [(w*LOADS + j)*1024, +1024) of a tile,
+    // lane i the 16 bytes at +16*i; the lane loads the global chunk that the
+    // swizzle puts there.  Rows at or past T read as zero (buffer range check).
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + slab, (uint32_t)T * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + slab, (uint32_t)T * ROWB);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int dma_src[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int pos = (wave * LOADS + j) * 1024 + lane * 16;
+        const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
+        dma_src[j] = row * ROWB + ((slot ^ tile_swz(row)) << 4);
+    }
+    auto gload = [&](int n, int buf) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            dma16(rk, &smem[buf][0][(wave_u * LOADS + j) * 1024], dma_src[j], n * TILEB);
+            dma16(rv, &smem[buf][1][(wave_u * LOADS + j) * 1024], dma_src[j], n * TILEB);
+        }
+    };
+
+    // operand read offsets (bytes within a tile)
+    int koff[NDS];  // K row kb*32 + l32, chunk 2*ds + hi
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz(l32)) << 4);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int vrow = 4 * (g16 >> 1) + (s16 >> 2);  // + kb*32 + 16c (+8 for the upper keys)
+    int voff[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        voff[dt] = vrow * ROWB + (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz(vrow)) << 4) +
+                   8 * (s16 & 1);
+
+    auto k_frag = [&](int buf, int kb, int ds) {
+        return *(const bf16x8 *)(&smem[buf][0][koff[ds] + kb * 32 * ROWB]);
+    };
+    // V^T operand for keys kb*32 + 16c + {4hi..4hi+3, 8+4hi..8+4hi+3}, dims 32dt + lane%32
+    auto v_frag = [&](int buf, int kb, int dt, int c) {
+        const uint8_t *base = &smem[buf][1][voff[dt] + (kb * 32 + 16 * c) * ROWB];
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base));
+        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + 8 * ROWB));
+        return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // weights of one S^T block (threshold and mask already applied), rounded to bf16
+    // in the register order of the two P^T operands
+    auto epilogue = [&](const f32x16 &sv, bf16x8 (&pf)[2]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(sv[r], p);
+    };
+
+    gload(0, 0);
+    __syncthreads();
+
+    // One 64-key tile = two 32-key blocks, in four phases:
+    //   A: S0 = -tau + K0 Q^T               (next tile's DMA into the other buffer)
+    //   B: S1 = -tau + K1 Q^T || epilogue(S0)
+    //   C: O += V0 P0         || epilogue(S1)
+    //   D: O += V1 P1
+    for (int n = 0; n < ntiles; ++n) {
+        const int buf = n & 1;
+        const bool diag = n * kBN + kBN - 1 > qw0;  // tile reaches past this wave's first row
+        bf16x8 ka[NDS], kb1[NDS], va[NDT][2], vb[NDT][2];
+        f32x16 s0[QB], s1[QB];
+        bf16x8 p0[QB][2], p1[QB][2];
+        // A
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) ka[ds] = k_frag(buf, 0, ds);
+        if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kb1[ds] = k_frag(buf, 1, ds);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s0[qb] = cinit[qb];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s0[qb] = mfma_32x32x16(ka[ds], qf[qb][ds], s0[qb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (diag) mask_block(s0, n * kBN);
+        // B
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) va[dt][c] = v_frag(buf, 0, dt, c);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s1[qb] = cinit[qb];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s1[qb] = mfma_32x32x16(kb1[ds], qf[qb][ds], s1[qb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) epilogue(s0[qb], p0[qb]);
+#pragma unroll
+        for (int i = 0; i < NDS * QB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // then VALU
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then an LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (diag) mask_block(s1, n * kBN + 32);
+        // C
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) vb[dt][c] = v_frag(buf, 1, dt, c);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[qb][dt] = mfma_32x32x16(va[dt][c], p0[qb][c], oacc[qb][dt]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) epilogue(s1[qb], p1[qb]);
+#pragma unroll
+        for (int i = 0; i < NDT * 2 * QB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // D
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[qb][dt] = mfma_32x32x16(vb[dt][c], p1[qb][c], oacc[qb][dt]);
+        __syncthreads();
+    }
+
+    // O^T accumulator: lane holds row qw0 + 32*qb + l32, dims 32*dt + 8*i + 4*hi + j.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int myq = qw0 + 32 * qb + l32;
+        if (myq < T) {
+            uint16_t *orow = O + slab + (size_t)myq * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 pr = {pack_bf16x2(oacc[qb][dt][4 * i], oacc[qb][dt][4 * i + 1]),
+                                      pack_bf16x2(oacc[qb][dt][4 * i + 2], oacc[qb][dt][4 * i + 3])};
+                    *(u32x2 *)(orow + dt * 32 + 8 * i + 4 * hi) = pr;
+                }
+        }
     }
 }
 
@@ -248,7 +314,7 @@ template <int D, int PM>
 __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, int T, int nqt, float beta, float p) {
-    constexpr int BQ = 64, BK = 64, DPT = D / 4;
+    constexpr int BQ = kTraF32Rows, BK = 64, DPT = D / 4;
     __shared__ float Ksh[BK][D];
     __shared__ float Vsh[BK][D];
 
@@ -298,16 +364,17 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
 template <int D, int PM>
 hipError_t launch_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                        int BH, int T, float beta, float p, hipStream_t stream) {
-    int nqt = (T + kBM - 1) / kBM;
+    constexpr int QB = kQueryBlocks;
+    int nqt = (T + 128 * QB - 1) / (128 * QB);
     void *args[] = {&q, &k, &v, &out, &BH, &T, &nqt, &beta, &p};
-    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM>,
+    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM, QB>,
                            dim3((unsigned)(BH * nqt)), dim3(kThreads), args, 0, stream);
 }
 
 template <int D, int PM>
 hipError_t launch_f32(const float *q, const float *k, const float *v, float *out, int BH,
                       int T, float beta, float p, hipStream_t stream) {
-    int nqt = (T + 63) / 64;
+    int nqt = (T + kTraF32Rows - 1) / kTraF32Rows;
     void *args[] = {&q, &k, &v, &out, &T, &nqt, &beta, &p};
     return hipLaunchKernel((const void *)tra_fwd_f32_kernel<D, PM>,
                            dim3((unsigned)(BH * nqt)), dim3(kThreads), args, 0, stream);
