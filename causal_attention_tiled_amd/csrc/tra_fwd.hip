@@ -24,6 +24,8 @@
 //  * Launch order: the heaviest query tiles (largest i) first, and the heads split
 //    into 8 contiguous groups so that each XCD (dispatch is round-robin over the 8
 //    XCDs) works on its own heads and keeps their K/V in its private L2.
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -103,9 +105,12 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
 
     int bh, qt;
     tra_tile_of(blockIdx.x, BH, nqt, bh, qt);
+    // workgroup-uniform: keep them (and the buffer resources built from them) scalar
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    qt = __builtin_amdgcn_readfirstlane(qt);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
     const size_t slab = (size_t)bh * T * D;
 
@@ -164,7 +169,6 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     // swizzle puts there.  Rows at or past T read as zero (buffer range check).
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + slab, (uint32_t)T * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + slab, (uint32_t)T * ROWB);
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     int dma_src[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -175,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     auto gload = [&](int n, int buf) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            dma16(rk, &smem[buf][0][(wave_u * LOADS + j) * 1024], dma_src[j], n * TILEB);
-            dma16(rv, &smem[buf][1][(wave_u * LOADS + j) * 1024], dma_src[j], n * TILEB);
+            dma16(rk, &smem[buf][0][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
+            dma16(rv, &smem[buf][1][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
         }
     };
 
@@ -217,9 +221,9 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     //   B: S1 = -tau + K1 Q^T || epilogue(S0)
     //   C: O += V0 P0         || epilogue(S1)
     //   D: O += V1 P1
-    for (int n = 0; n < ntiles; ++n) {
+    auto tile = [&](int n, auto masked) {
+        constexpr bool kMasked = decltype(masked)::value;
         const int buf = n & 1;
-        const bool diag = n * kBN + kBN - 1 > qw0;  // tile reaches past this wave's first row
         bf16x8 ka[NDS], kb1[NDS], va[NDT][2], vb[NDT][2];
         f32x16 s0[QB], s1[QB];
         bf16x8 p0[QB][2], p1[QB][2];
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s0[qb] = mfma_32x32x16(ka[ds], qf[qb][ds], s0[qb]);
         __builtin_amdgcn_sched_barrier(0);
-        if (diag) mask_block(s0, n * kBN);
+        if constexpr (kMasked) mask_block(s0, n * kBN);
         // B
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // then an LDS read
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (diag) mask_block(s1, n * kBN + 32);
+        if constexpr (kMasked) mask_block(s1, n * kBN + 32);
         // C
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -288,7 +292,14 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
                 for (int qb = 0; qb < QB; ++qb)
                     oacc[qb][dt] = mfma_32x32x16(vb[dt][c], p1[qb][c], oacc[qb][dt]);
         __syncthreads();
-    }
+    };
+    // Tiles entirely at or below this wave's first row need no mask; the rest
+    // (diagonal, past the wave's rows, or past T) take the masked body.  Every wave
+    // runs ntiles iterations, so the barriers stay matched.
+    const int n_interior = min(ntiles, (qw0 + 1) / kBN);
+    int n = 0;
+    for (; n < n_interior; ++n) tile(n, std::false_type{});
+    for (; n < ntiles; ++n) tile(n, std::true_type{});
 
     // O^T accumulator: lane holds row qw0 + 32*qb + l32, dims 32*dt + 8*i + 4*hi + j.
 #pragma unroll
