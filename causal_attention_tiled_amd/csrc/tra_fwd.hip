@@ -66,25 +66,45 @@ __device__ __forceinline__ void tra_tile_of(int bid, int BH, int nqt, int &bh, i
 }
 
 // LDS tile layout (K and V alike): row-major [key][dim], D*2 bytes per row, no
-// padding; the 16-byte chunk c of row r sits in chunk slot c ^ tile_swz(r).  With
-// this swizzle the 8 rows read by 8 consecutive lanes (K operand, ds_read_b128) and
-// the 4 rows x 32 bytes read by a 16-lane group (V operand, ds_read_b64_tr_b16) each
-// cover all banks once.
-__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// padding; the 16-byte chunk c of row r sits in chunk slot c ^ tile_swz<D>(r).  The
+// LDS has 64 four-byte banks (256 bytes per cycle).  With this swizzle the 16 rows
+// that 16 consecutive lanes read for the K operand (ds_read_b128), and the 4 rows x
+// 64 bytes that 32 lanes read for the V operand (ds_read_b64_tr_b16), each cover
+// all 64 banks once.
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+    if constexpr (D == 128)  // one row per bank line, 16 chunk slots
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    else                     // two 128-byte rows per bank line, 8 chunk slots
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
-// Raw buffer resource over `bytes` bytes at `base`; loads past the end return 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
+// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`, held in scalar
+// registers; loads past the end return 0.
+__device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu), bytes,
+               0x00020000u};
+    return r;
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+// 16 bytes per lane from global memory (resource + voff + soff) straight into LDS at
+// lds + 16 * lane.  Issued as inline assembly so that the compiler does not add its
+// own (conservative) waits for it before unrelated LDS reads: completion is awaited
+// explicitly, with s_waitcnt vmcnt, before the barrier that publishes the tile.
+// M0 carries the LDS address and is set here for each transfer.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(u32x4 rsrc, void *lds, int voff, int soff) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 template <int D, int PM, int QB>
 __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
@@ -101,7 +121,12 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     static_assert(LOADS >= 1 && kBN * CH % kThreads == 0, "tile staging");
     static_assert(TILEB == 4 * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][TILEB];  // [buffer][K, V]
+    // Two LDS buffers, each holding the K and V tiles of one 64-key tile: tile n
+    // lives in lds_a when n is even and in lds_b when n is odd, and is fetched one
+    // tile ahead, while the previous tile is being consumed.
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TILEB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TILEB];
+    typedef uint8_t TileBuf[2][TILEB];
 
     int bh, qt;
     tra_tile_of(blockIdx.x, BH, nqt, bh, qt);
@@ -120,29 +145,6 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     const int q_last = min(q0 + BM, T) - 1;
     const int ntiles = q_last / kBN + 1;
 
-    // Q^T operands and thresholds
-    bf16x8 qf[QB][NDS];
-    float tau[QB];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int myq = qw0 + 32 * qb + l32;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            u32x4 r = zero4;
-            if (myq < T) r = *(const u32x4 *)(Q + slab + (size_t)myq * D + ds * 16 + hi * 8);
-            qf[qb][ds] = as_bf16x8(r);
-        }
-        tau[qb] = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
-    }
-
-    // S^T accumulators start from -tau of the lane's row, so the epilogue never
-    // subtracts the threshold.
-    f32x16 cinit[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cinit[qb][r] = -tau[qb];
     // Causal mask of one 32-key block starting at kbase (only for blocks that reach
     // past this wave's first row): register r holds key kbase + 8*(r/4) + 4*hi + r%4.
     auto mask_block = [&](f32x16 (&sv)[QB], int kbase) {
@@ -167,43 +169,48 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
     // Instruction j of wave w fills LDS bytes [(w*LOADS + j)*1024, +1024) of a tile,
     // lane i the 16 bytes at +16*i; the lane loads the global chunk that the
     // swizzle puts there.  Rows at or past T read as zero (buffer range check).
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + slab, (uint32_t)T * ROWB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + slab, (uint32_t)T * ROWB);
+    const u32x4 rk = make_rsrc(K + slab, (uint32_t)T * ROWB);
+    const u32x4 rv = make_rsrc(V + slab, (uint32_t)T * ROWB);
     int dma_src[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
         const int pos = (wave * LOADS + j) * 1024 + lane * 16;
         const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
-        dma_src[j] = row * ROWB + ((slot ^ tile_swz(row)) << 4);
+        dma_src[j] = row * ROWB + ((slot ^ tile_swz<D>(row)) << 4);
     }
-    auto gload = [&](int n, int buf) {
+    auto gload = [&](int n, TileBuf &dst) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            dma16(rk, &smem[buf][0][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
-            dma16(rv, &smem[buf][1][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
+            dma16(rk, &dst[0][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
+            dma16(rv, &dst[1][(wave * LOADS + j) * 1024], dma_src[j], n * TILEB);
         }
     };
 
     // operand read offsets (bytes within a tile)
     int koff[NDS];  // K row kb*32 + l32, chunk 2*ds + hi
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz(l32)) << 4);
+    for (int ds = 0; ds < NDS; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz<D>(l32)) << 4);
     const int g16 = lane >> 4, s16 = lane & 15;
-    const int vrow = 4 * (g16 >> 1) + (s16 >> 2);  // + kb*32 + 16c (+8 for the upper keys)
-    int voff[NDT];
+    const int vrow = 4 * (g16 >> 1) + (s16 >> 2);  // + kb*32 + 16c, + 8 for the upper keys
+    int voff[NDT][2];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
-        voff[dt] = vrow * ROWB + (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz(vrow)) << 4) +
-                   8 * (s16 & 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = vrow + 8 * h;
+            voff[dt][h] = row * ROWB +
+                          (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
+                          8 * (s16 & 1);
+        }
 
-    auto k_frag = [&](int buf, int kb, int ds) {
-        return *(const bf16x8 *)(&smem[buf][0][koff[ds] + kb * 32 * ROWB]);
+    auto k_frag = [&](const TileBuf &t, int kb, int ds) {
+        return *(const bf16x8 *)(&t[0][koff[ds] + kb * 32 * ROWB]);
     };
     // V^T operand for keys kb*32 + 16c + {4hi..4hi+3, 8+4hi..8+4hi+3}, dims 32dt + lane%32
-    auto v_frag = [&](int buf, int kb, int dt, int c) {
-        const uint8_t *base = &smem[buf][1][voff[dt] + (kb * 32 + 16 * c) * ROWB];
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base));
-        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + 8 * ROWB));
+    auto v_frag = [&](const TileBuf &t, int kb, int dt, int c) {
+        const uint8_t *base = &t[1][(kb * 32 + 16 * c) * ROWB];
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][0]));
+        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + voff[dt][1]));
         return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     // weights of one S^T block (threshold and mask already applied), rounded to bf16
@@ -213,24 +220,58 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) pf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(sv[r], p);
     };
 
-    gload(0, 0);
-    __syncthreads();
+    // End-of-tile synchronisation: each wave waits for its own DMAs (the next tile)
+    // and its own LDS reads (of this tile), then all waves meet.  After the barrier
+    // the next tile is complete in LDS and nobody reads the buffer that the next
+    // DMA overwrites.
+    auto tile_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    };
+
+    gload(0, lds_a);
+    // Q^T operands and thresholds (loaded while the first tile streams in)
+    bf16x8 qf[QB][NDS];
+    float tau[QB];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int myq = qw0 + 32 * qb + l32;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 r = zero4;
+            if (myq < T) r = *(const u32x4 *)(Q + slab + (size_t)myq * D + ds * 16 + hi * 8);
+            qf[qb][ds] = as_bf16x8(r);
+        }
+        tau[qb] = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
+    }
+
+    // S^T accumulators start from -tau of the lane's row, so the epilogue never
+    // subtracts the threshold.
+    f32x16 cinit[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cinit[qb][r] = -tau[qb];
+    // Drain everything once: the first tiles have landed and the Q operands are in
+    // registers, so nothing issued before the loop is waited on inside it.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
 
     // One 64-key tile = two 32-key blocks, in four phases:
-    //   A: S0 = -tau + K0 Q^T               (next tile's DMA into the other buffer)
+    //   A: S0 = -tau + K0 Q^T               (DMA of the next tile issued)
     //   B: S1 = -tau + K1 Q^T || epilogue(S0)
     //   C: O += V0 P0         || epilogue(S1)
     //   D: O += V1 P1
-    auto tile = [&](int n, auto masked) {
+    auto tile = [&](int n, auto masked, const TileBuf &buf, TileBuf &next) {
         constexpr bool kMasked = decltype(masked)::value;
-        const int buf = n & 1;
         bf16x8 ka[NDS], kb1[NDS], va[NDT][2], vb[NDT][2];
         f32x16 s0[QB], s1[QB];
         bf16x8 p0[QB][2], p1[QB][2];
         // A
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) ka[ds] = k_frag(buf, 0, ds);
-        if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
+        if (n + 1 < ntiles) gload(n + 1, next);
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) kb1[ds] = k_frag(buf, 1, ds);
 #pragma unroll
@@ -291,15 +332,26 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     oacc[qb][dt] = mfma_32x32x16(vb[dt][c], p1[qb][c], oacc[qb][dt]);
-        __syncthreads();
+        tile_sync();
     };
     // Tiles entirely at or below this wave's first row need no mask; the rest
     // (diagonal, past the wave's rows, or past T) take the masked body.  Every wave
     // runs ntiles iterations, so the barriers stay matched.
     const int n_interior = min(ntiles, (qw0 + 1) / kBN);
+    const std::false_type plain{};
+    const std::true_type masked{};
     int n = 0;
-    for (; n < n_interior; ++n) tile(n, std::false_type{});
-    for (; n < ntiles; ++n) tile(n, std::true_type{});
+    for (; n + 1 < n_interior; n += 2) {
+        tile(n, plain, lds_a, lds_b);
+        tile(n + 1, plain, lds_b, lds_a);
+    }
+    if (n < n_interior) tile(n++, plain, lds_a, lds_b);
+    if (n < ntiles && (n & 1)) tile(n++, masked, lds_b, lds_a);
+    for (; n + 1 < ntiles; n += 2) {
+        tile(n, masked, lds_a, lds_b);
+        tile(n + 1, masked, lds_b, lds_a);
+    }
+    if (n < ntiles) tile(n++, masked, lds_a, lds_b);
 
     // O^T accumulator: lane holds row qw0 + 32*qb + l32, dims 32*dt + 8*i + 4*hi + j.
 #pragma unroll
