@@ -31,9 +31,10 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kQueryBlocks = 2;  // 32-row query blocks per wave (64 rows per wave)
-static_assert(4 * 32 * kQueryBlocks == kTraBf16Rows, "workgroup rows");
+constexpr int kThreads = 256;    // fp32 kernel
+constexpr int kQueryBlocks = 1;  // bf16 kernel: 32-row query blocks per wave
+constexpr int kWaves = 8;        // bf16 kernel: wavefronts per workgroup
+static_assert(kWaves * 32 * kQueryBlocks == kTraBf16Rows, "workgroup rows");
 constexpr int kBN = 64;   // keys per LDS tile
 
 enum PowMode { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2 };
@@ -106,20 +107,20 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, void *lds, int voff, int soff)
 }
 #pragma clang diagnostic pop
 
-template <int D, int PM, int QB>
-__global__ __launch_bounds__(kThreads) void tra_fwd_bf16_kernel(
+template <int D, int PM, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, uint16_t *__restrict__ O, int BH, int T, int nqt,
     float beta, float p) {
-    constexpr int BM = 4 * 32 * QB;             // query rows per workgroup
+    constexpr int BM = NW * 32 * QB;            // query rows per workgroup
     constexpr int ROWB = D * 2;                 // bytes per key row
     constexpr int CH = D / 8;                   // 16-byte chunks per row
     constexpr int TILEB = kBN * ROWB;           // bytes of one K (or V) tile
-    constexpr int LOADS = kBN * CH / kThreads;  // 16-byte chunks per thread per tensor
+    constexpr int LOADS = kBN * CH / (64 * NW); // 16-byte chunks per thread per tensor
     constexpr int NDS = D / 16;                 // S^T MFMA k-steps
     constexpr int NDT = D / 32;                 // 32-dim output tiles
-    static_assert(LOADS >= 1 && kBN * CH % kThreads == 0, "tile staging");
-    static_assert(TILEB == 4 * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
+    static_assert(LOADS >= 1 && kBN * CH % (64 * NW) == 0, "tile staging");
+    static_assert(TILEB == NW * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
 
     // Two LDS buffers, each holding the K and V tiles of one 64-key tile: tile n
     // lives in lds_a when n is even and in lds_b when n is odd, and is fetched one
@@ -427,11 +428,10 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
 template <int D, int PM>
 hipError_t launch_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                        int BH, int T, float beta, float p, hipStream_t stream) {
-    constexpr int QB = kQueryBlocks;
-    int nqt = (T + 128 * QB - 1) / (128 * QB);
+    int nqt = (T + kTraBf16Rows - 1) / kTraBf16Rows;
     void *args[] = {&q, &k, &v, &out, &BH, &T, &nqt, &beta, &p};
-    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM, QB>,
-                           dim3((unsigned)(BH * nqt)), dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM, kQueryBlocks, kWaves>,
+                           dim3((unsigned)(BH * nqt)), dim3(64 * kWaves), args, 0, stream);
 }
 
 template <int D, int PM>
