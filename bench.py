@@ -36,6 +36,13 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 
 TRA = dict(B=2, H=32, T=8192, D=128, beta=1.0, p=2.0)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "causal_attention_tiled_amd", "csrc")
+# sources whose change invalidates a recorded traffic figure of each kernel
+KERNEL_SOURCES = {
+    "tra_fwd": ["tra_fwd.hip", "attn_internal.h"],
+    "nsa_sel_fwd": ["nsa_sel_fwd.hip", "attn_internal.h"],
+}
 NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
 
 
@@ -63,6 +70,29 @@ def nsa_gathered_bytes(idx, T, bs, D, rows_kv=None):
     distinct = (srt >= 0) & np.concatenate([np.ones((srt.shape[0], 1), bool),
                                             srt[:, 1:] != srt[:, :-1]], axis=1)
     return float(distinct.sum()) * 2 * bs * D * 2
+
+
+def kernel_source_hash(name):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[name] + ["../build.py"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch recorded in profiles/hbm_traffic.txt for `name`, or None
+    when there is no record or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("kernel="):
+            continue
+        kv = dict(item.split("=", 1) for item in line.split())
+        if kv.get("kernel") == name and kv.get("source") == kernel_source_hash(name):
+            return float(kv["traffic_bytes"])
+    return None
 
 
 def cpu_baseline(q, k, v, idx_np, budget_s=12.0):
@@ -117,7 +147,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["tra", "nsa"], default=None,
                     help="launch only one of the two forwards (for profiling runs)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run a plain device copy of this many bytes (3 times), the "
+                         "reference for calibrating HBM traffic counters")
+    ap.add_argument("--source-hashes", action="store_true",
+                    help="print the source hash of each kernel and exit")
     args = ap.parse_args()
+    if args.source_hashes:
+        for name in KERNEL_SOURCES:
+            print(name, kernel_source_hash(name))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the forwards are single-GPU kernels; sharding is described, not run)",
@@ -141,6 +180,15 @@ def main():
     o_n = torch.empty_like(gqn)
     lse_n = torch.empty(NSA["B"], NSA["Hq"], NSA["T"], dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)          # reads and writes exactly copy_bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     run_tra = args.only in (None, "tra")
     run_nsa = args.only in (None, "nsa")
@@ -183,11 +231,11 @@ def main():
 
     roof_tra = {"kernel": "tra_fwd_bf16_kernel<128,p=2>", "bound": "mfma",
                 "achieved": tra_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tra_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": tra_tflops / PEAK_BF16_TFLOPS, "traffic": recorded_traffic("tra_fwd"),
                 "per_launch": f"{flops:.6g} useful FLOPs / {tra_avg:.4f} ms avg launch"}
     roof_nsa = {"kernel": "nsa_sel_fwd_kernel<128,64>", "bound": "hbm",
                 "achieved": nsa_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": nsa_gbps / PEAK_HBM_GBPS, "traffic": None,
+                "frac": nsa_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic("nsa_sel_fwd"),
                 "per_launch": f"{gbytes:.6g} gathered K/V bytes / {nsa_avg:.4f} ms avg launch"}
     dominant = roof_nsa if nsa_avg >= tra_avg else roof_tra
 

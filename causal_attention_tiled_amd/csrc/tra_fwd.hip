@@ -273,6 +273,13 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) ka[ds] = k_frag(buf, 0, ds);
         if (n + 1 < ntiles) gload(n + 1, next);
+        if constexpr (kMasked) {
+            // every key of the tile lies after every row of this wave: nothing to add
+            if (n * kBN > qw0 + 32 * QB - 1) {
+                tile_sync();
+                return;
+            }
+        }
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) kb1[ds] = k_frag(buf, 1, ds);
 #pragma unroll
