@@ -67,6 +67,7 @@ ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
     if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 32 && block_size != 64 && block_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+    if (S > 64) return ATTN_ERR_UNSUPPORTED;
     if (T % block_size != 0) return ATTN_ERR_SHAPE;
     if (B == 0 || Hq == 0 || T == 0) return ATTN_OK;
     if (!q || !k || !v || !block_idx || !out) return ATTN_ERR_NULL;

@@ -12,18 +12,23 @@
 //    queries of one group.  The G query heads of the group are packed into the N
 //    dimension of v_mfma_f32_16x16x32_bf16, so every gathered K/V tile is read once
 //    per group, not once per head.
-//  * The wave walks the S slots of its block_idx row (wave-uniform scalar loads),
-//    skipping padding, blocks past T/bs, blocks entirely after i and repeats of an
-//    earlier slot.  No scan over the KV sequence takes place.
-//  * Scores are computed transposed, S^T = K Q^T: K streams straight from global
-//    memory into the A operand (16 keys x 32 dims per MFMA), Q^T sits in registers.
-//    Each lane then holds ONE head (lane % 16) and 16 keys, so the online-softmax
-//    state (running max, partial sum, output rescale) is per-lane scalar work plus a
-//    two-step cross-lane max.
-//  * The exponentials (base 2, scale*log2e folded in) are rounded to bf16 and, in
-//    accumulator register order, form the B operand of O^T += V^T P^T.  V^T comes
-//    from a per-wave LDS tile written transposed from the gathered V rows; the key
-//    order implied by the accumulator layout is folded into that LDS layout.
+//  * The S slots of the query's block_idx row are validated lane-parallel (lane s
+//    holds slot s): padding, ids past T/bs, blocks after i and repeats of an earlier
+//    slot are dropped, and the survivors form a bit mask that the wave walks.  No
+//    scan over the KV sequence takes place.
+//  * Keys are processed in chunks of 32.  The next chunk is fetched while the
+//    current one is computed: its K rows go straight into the MFMA A-operand
+//    registers (buffer loads with a scalar chunk offset), its V rows are copied by
+//    the memory unit straight into one of two per-wave LDS tiles (two separate LDS
+//    objects, used alternately).
+//  * Scores are computed transposed, S^T = K Q^T, so each lane holds ONE head (lane %
+//    16): the online-softmax state (running max in base-2 units, per-lane partial
+//    sum, output rescale) is per-lane work plus a two-step cross-lane max.  Only the
+//    chunk that holds position i is masked.
+//  * The exponentials, rounded to bf16, form in accumulator register order the B
+//    operand of O^T += V^T P^T; the V^T operand is read from the row-major LDS tile
+//    with ds_read_b64_tr_b16 (in each 16-lane group, output lane i, value t is
+//    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).
 //  * Workgroup order keeps each XCD on a contiguous range of (group, query) work so a
 //    group's K/V stays in one XCD's L2.
 #include "attn_internal.h"
@@ -33,20 +38,40 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kChunk = 32;  // keys per processed chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// V^T chunk in LDS: row = head dim, column = key position within a chunk of KC keys.
-// In every 32-key group the key offset o = 16a + 4g + j is stored at 8g + 4a + j, so
-// that the 8 keys a lane feeds to one 16x16x32 MFMA are contiguous.  4-key units are
-// XOR-swizzled by an even, row-dependent amount to spread the transposing writes.
-__device__ __forceinline__ int nsa_vt_pos(int o) {
-    return (o & ~31) | (((o >> 2) & 3) << 3) | (((o >> 4) & 1) << 2) | (o & 3);
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 layout, range-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nsa_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
-template <int NU>
-__device__ __forceinline__ int nsa_vt_offset(int row, int pos, int stride) {
-    const int unit = (pos >> 2) ^ ((row >> 2) & (NU - 2));
-    return row * stride + (unit << 2) + (pos & 3);
+
+// 16 bytes per lane from (resource, voff + soff) into LDS at lds + 16 * lane.
+__device__ __forceinline__ void nsa_dma16(__amdgpu_buffer_rsrc_t r, void *lds, int voff,
+                                          int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Wait until this wave's LDS reads have returned (lgkmcnt(0); vmcnt and expcnt
+// untouched), so that an LDS tile it just read may be refilled.
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// V chunk in LDS: 32 rows (keys) x D*2 bytes, row-major; the 16-byte chunk c of row r
+// sits at chunk slot c ^ nsa_swz<D>(r).  A 16-lane group of the transposing read
+// takes 4 consecutive rows x 32 bytes; with this swizzle the 32 lanes served per
+// cycle (8 rows) cover all 64 banks once.
+template <int D>
+__device__ __forceinline__ int nsa_swz(int row) {
+    if constexpr (D == 128)
+        return (row & 7) << 1;          // one row per 256-byte bank line
+    else
+        return ((row >> 1) & 3) << 1;   // two rows per bank line
 }
 
 template <int D, int BS>
@@ -55,19 +80,16 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
     const uint16_t *__restrict__ V, const int32_t *__restrict__ IDX, uint16_t *__restrict__ O,
     float *__restrict__ LSE, int Hq, int Hkv, int G, int T, int S, int nq4, int ngroups,
     float score_scale) {
-    constexpr int KC = BS < 64 ? BS : 64;  // keys per processed chunk
-    constexpr int NCH = BS / KC;           // chunks per selected block
-    constexpr int NKK = KC / 16;           // 16-key sub-tiles (S^T MFMA rows)
-    constexpr int NPV = KC / 32;           // 32-key PV steps
-    constexpr int NDS = D / 32;            // S^T MFMA k-steps
-    constexpr int NDT = D / 16;            // 16-dim output tiles
-    constexpr int VSTR = KC + 8;           // V^T row stride (elements)
-    constexpr int NU = KC / 4;             // 4-key units per V^T row
-    constexpr int DC = D / 8;              // 16-byte chunks per row
-    constexpr int VPL = (KC / 4) * DC / 64;  // 4-key x 8-dim V blocks per lane
-    static_assert(VPL >= 1 && (KC / 4) * DC % 64 == 0, "V blocks must tile the wave");
+    constexpr int ROWB = D * 2;              // bytes per key row
+    constexpr int NCH = BS / kChunk;         // chunks per selected block
+    constexpr int NDS = D / 32;              // S^T MFMA k-steps
+    constexpr int NDT = D / 16;              // 16-dim output tiles
+    constexpr int VTILE = kChunk * ROWB;     // bytes of one V chunk
+    constexpr int VDMA = VTILE / 1024;       // 1 KB DMA instructions per chunk
+    static_assert(BS % kChunk == 0 && VTILE % 1024 == 0, "chunking");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[kWaves][D * VSTR];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf_a[kWaves][VTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf_b[kWaves][VTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -78,13 +100,24 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
     const int W = ngroups * nq4;
     int f = blockIdx.x;
     if ((W & 7) == 0) f = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
-    const int group = f / nq4;
-    const int i = (nq4 - 1 - f % nq4) * kWaves + wave;  // later (busier) queries first
+    const int group = __builtin_amdgcn_readfirstlane(f / nq4);
+    const int i = __builtin_amdgcn_readfirstlane((nq4 - 1 - f % nq4) * kWaves + wave);
     if (i >= T) return;  // no workgroup-wide barrier in this kernel
     const int b = group / Hkv, kv = group % Hkv;
     const size_t kvslab = (size_t)group * T * D;
+    const __amdgpu_buffer_rsrc_t rk = nsa_rsrc(K + kvslab, (uint32_t)T * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = nsa_rsrc(V + kvslab, (uint32_t)T * ROWB);
+
+    // ---- the selected blocks: lane s holds slot s (S <= 64) ----
+    const int nblk = T / BS;
     const int32_t *slots = IDX + ((size_t)group * T + i) * S;
-    uint16_t *vts = Vs[wave];
+    const int myblk = lane < S ? slots[lane] : -1;
+    bool keep = myblk >= 0 && myblk < nblk && myblk * BS <= i;
+    for (int s2 = 0; s2 < S; ++s2) {  // drop repeats of an earlier slot
+        const int other = __builtin_amdgcn_readlane(myblk, s2);
+        keep = keep && !(s2 < lane && other == myblk);
+    }
+    uint64_t rem = __builtin_amdgcn_ballot_w64(keep);
 
     // Q^T operand: head kv*G + n16 (zero for n16 >= G), dims 32*ds + 8*g4 .. +7
     const bool head_ok = n16 < G;
@@ -100,117 +133,131 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
         }
     }
 
+    // ---- per-lane load offsets (bytes within a chunk) ----
+    const int koff = n16 * ROWB + g4 * 16;  // K row 16*kk + n16, dims 32*ds + 8*g4
+    int vdma_off[VDMA];                     // V rows written by DMA instruction j
+#pragma unroll
+    for (int j = 0; j < VDMA; ++j) {
+        const int pos = j * 1024 + lane * 16;
+        const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
+        vdma_off[j] = row * ROWB + ((slot ^ nsa_swz<D>(row)) << 4);
+    }
+    // V^T operand reads: rows 4*g4 + s/4 (+16 for the upper keys), dims 16*dt + 4*(s%4)
+    const int s16 = n16;
+    int vrd_off[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * g4 + (s16 >> 2) + 16 * h;
+            const int col = 16 * dt + 4 * (s16 & 3);  // element
+            vrd_off[dt][h] = row * ROWB + (((col >> 3) ^ nsa_swz<D>(row)) << 4) + (col & 7) * 2;
+        }
+
+    typedef uint8_t VTile[kWaves][VTILE];
+    bf16x8 kfa[2][NDS], kfb[2][NDS];  // K operands of the two chunks in flight
+
+    auto load_chunk = [&](int k0, bf16x8 (&kf)[2][NDS], VTile &vt) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds)
+                kf[kk][ds] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                rk, koff + ds * 64, (k0 + 16 * kk) * ROWB, 0));
+#pragma unroll
+        for (int j = 0; j < VDMA; ++j) nsa_dma16(rv, &vt[wave][j * 1024], vdma_off[j], k0 * ROWB);
+    };
+
     float m = -INFINITY;  // running max of the base-2 scores (this lane's head)
     float lsum = 0.0f;    // this lane's share of the running sum
     f32x4 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nblk = T / BS;
-    for (int s = 0; s < S; ++s) {
-        const int blk = slots[s];
-        if (blk < 0 || blk >= nblk || blk * BS > i) continue;
-        bool dup = false;
-        for (int s2 = 0; s2 < s; ++s2) dup |= (slots[s2] == blk);
-        if (dup) continue;
-
-#pragma unroll 1
-        for (int ch = 0; ch < NCH; ++ch) {
-            const int k0 = blk * BS + ch * KC;
-            if (k0 > i) break;
-            const int nvalid = min(KC, i - k0 + 1);  // keys k0 .. k0+nvalid-1 are causal
-
-            // gather K (MFMA A operand, straight from global) and V (rows, for LDS)
-            u32x4 kf[NKK][NDS];
+    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const VTile &vt) {
+        // S^T = K Q^T : register j of st[kk] is key k0 + 16*kk + 4*g4 + j, head n16
+        f32x4 st[2];
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
+        for (int kk = 0; kk < 2; ++kk) {
+            st[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ds = 0; ds < NDS; ++ds)
-                    kf[kk][ds] = *(const u32x4 *)(K + kvslab + (size_t)(k0 + kk * 16 + n16) * D +
-                                                  ds * 32 + g4 * 8);
-            u32x4 vr[VPL][4];
-#pragma unroll
-            for (int r = 0; r < VPL; ++r) {
-                const int blkid = lane + 64 * r;
-                const int kg = blkid / DC, dc = blkid % DC;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    vr[r][e] = *(const u32x4 *)(V + kvslab + (size_t)(k0 + kg * 4 + e) * D + dc * 8);
-            }
-
-            // S^T = K Q^T : register j of st[kk] is key k0 + 16*kk + 4*g4 + j, head n16
-            f32x4 st[NKK];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) {
-                st[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds)
-                    st[kk] = mfma_16x16x32(as_bf16x8(kf[kk][ds]), qf[ds], st[kk]);
-            }
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float t = st[kk][j] * score_scale;
-                    if (kk * 16 + g4 * 4 + j >= nvalid) t = -INFINITY;
-                    st[kk][j] = t;
-                    mloc = fmaxf(mloc, t);
-                }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float mnew = fmaxf(m, mloc);  // finite: key k0 is always causal
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            m = mnew;
-            float psum = 0.0f;
-            bf16x8 pf[NPV];
-#pragma unroll
-            for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float e = __builtin_amdgcn_exp2f(st[kk][j] - mnew);
-                    psum += e;
-                    pf[kk >> 1][(kk & 1) * 4 + j] = (__bf16)e;
-                }
-            lsum = lsum * alpha + psum;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-
-            // V rows -> V^T in this wave's LDS tile (after every lane has finished
-            // reading the previous chunk)
-            wave_lds_sync();
-#pragma unroll
-            for (int r = 0; r < VPL; ++r) {
-                const int blkid = lane + 64 * r;
-                const int kg = blkid / DC, dc = blkid % DC;
-                const int pos = nsa_vt_pos(kg * 4);
-#pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    const int w = d >> 1;
-                    uint32_t lo, hi2;
-                    if (d & 1) {
-                        lo = (vr[r][0][w] >> 16) | (vr[r][1][w] & 0xffff0000u);
-                        hi2 = (vr[r][2][w] >> 16) | (vr[r][3][w] & 0xffff0000u);
-                    } else {
-                        lo = (vr[r][0][w] & 0xffffu) | (vr[r][1][w] << 16);
-                        hi2 = (vr[r][2][w] & 0xffffu) | (vr[r][3][w] << 16);
-                    }
-                    const u32x2 pr = {lo, hi2};
-                    *(u32x2 *)(&vts[nsa_vt_offset<NU>(dc * 8 + d, pos, VSTR)]) = pr;
-                }
-            }
-            wave_lds_sync();
-
-            // O^T += V^T P^T : register j of oacc[dt] is dim 16*dt + 4*g4 + j, head n16
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int c = 0; c < NPV; ++c) {
-                    const bf16x8 a = *(const bf16x8 *)(&vts[nsa_vt_offset<NU>(
-                        dt * 16 + n16, c * 32 + g4 * 8, VSTR)]);
-                    oacc[dt] = mfma_16x16x32(a, pf[c], oacc[dt]);
-                }
+            for (int ds = 0; ds < NDS; ++ds) st[kk] = mfma_16x16x32(kf[kk][ds], qf[ds], st[kk]);
         }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) st[kk] *= score_scale;
+        if (k0 + kChunk - 1 > i) {  // the chunk holding position i: mask later keys
+            const int lim = i - k0 - 4 * g4;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (16 * kk + j > lim) st[kk][j] = -INFINITY;
+        }
+        float mloc = fmaxf(fmaxf(fmaxf(st[0][0], st[0][1]), fmaxf(st[0][2], st[0][3])),
+                           fmaxf(fmaxf(st[1][0], st[1][1]), fmaxf(st[1][2], st[1][3])));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float mnew = fmaxf(m, mloc);  // finite: key k0 <= i is never masked
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        float psum = 0.0f;
+        bf16x8 pf;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(st[kk][j] - mnew);
+                psum += e;
+                pf[kk * 4 + j] = (__bf16)e;
+            }
+        lsum = lsum * alpha + psum;
+        // O^T += V^T P^T : register j of oacc[dt] is dim 16*dt + 4*g4 + j, head n16
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const uint8_t *base = &vt[wave][0];
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4 *)(base + vrd_off[dt][0]));
+            const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4 *)(base + vrd_off[dt][1]));
+            const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[dt] = mfma_16x16x32(a, pf, oacc[dt] * alpha);
+        }
+    };
+
+    // Walk the chunks of the kept blocks in slot order: chunk (blk, c) starts at key
+    // blk*BS + 32*c and exists while it starts at or before i.
+    int cur_blk = -1, cur_c = 0;
+    auto next_chunk = [&]() -> int {
+        if (cur_blk >= 0 && cur_c + 1 < NCH && cur_blk * BS + (cur_c + 1) * kChunk <= i) {
+            ++cur_c;
+            return cur_blk * BS + cur_c * kChunk;
+        }
+        if (rem == 0) return -1;
+        const int s = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        cur_blk = __builtin_amdgcn_readlane(myblk, s);
+        cur_c = 0;
+        return cur_blk * BS;
+    };
+
+    // chunks alternate between (kfa, vbuf_a) and (kfb, vbuf_b); each is fetched one
+    // chunk ahead of its use
+    int ka = next_chunk();
+    if (ka >= 0) load_chunk(ka, kfa, vbuf_a);
+    int kb = ka >= 0 ? next_chunk() : -1;
+    while (ka >= 0) {
+        if (kb >= 0) load_chunk(kb, kfb, vbuf_b);
+        compute_chunk(ka, kfa, vbuf_a);
+        if (kb < 0) break;
+        ka = next_chunk();
+        if (ka >= 0) {
+            wait_lds_reads();  // this wave's reads of vbuf_a are done before it is refilled
+            load_chunk(ka, kfa, vbuf_a);
+        }
+        compute_chunk(kb, kfb, vbuf_b);
+        kb = ka >= 0 ? next_chunk() : -1;
+        if (kb >= 0) wait_lds_reads();  // likewise for vbuf_b
     }
 
     // finalize: total sum of this head over its 4 lanes

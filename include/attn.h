@@ -104,7 +104,7 @@ int tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
  *   Hq % Hkv   : must be 0                     (else ATTN_ERR_SHAPE)
  *   G = Hq/Hkv : 1 .. 16                       (else ATTN_ERR_UNSUPPORTED)
  *   T          : a multiple of block_size      (else ATTN_ERR_SHAPE)
- *   S          : >= 1                          (else ATTN_ERR_SHAPE)
+ *   S          : 1 .. 64                       (< 1: ATTN_ERR_SHAPE, > 64: ATTN_ERR_UNSUPPORTED)
  *
  * Numerics: scores in fp32 from bf16 products; softmax state (running max,
  * sum, accumulator) in fp32; probabilities rounded to bf16 before they

@@ -83,6 +83,7 @@ def test_nsa_validation(lib):
     assert _nsa(lib, Hkv=0) == ESHAPE
     assert _nsa(lib, T=100) == ESHAPE                # T % block_size
     assert _nsa(lib, S=0) == ESHAPE
+    assert _nsa(lib, S=65) == EUNSUP
     assert _nsa(lib, bs=16) == EUNSUP
     assert _nsa(lib, bs=48) == EUNSUP
     assert _nsa(lib, D=32) == EUNSUP
