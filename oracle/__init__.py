@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the two causal-attention forwards -- TEST INFRASTRUCTURE.
+"""fp64 CPU oracle for the causal-attention forwards -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never calls it, and it
@@ -10,6 +10,11 @@ Functions
     Threshold Rectified Attention, out_i = sum_{j<=i} ReLU(q_i.k_j - tau_i)^p v_j,
     tau_i = beta*sqrt(2 ln(i+1)/D).  Source: snap-research/TDA page
     "triton_threshold_attention.py", module docstring and the forward kernel.
+``tda_ref(q1, q2, k1, k2, v, beta, lam, p, normalize=True, rows=None)``
+    Threshold Differential Attention: optional L2 normalisation of the q and k
+    rows, two Threshold Rectified Attention outputs over the same v, combined
+    as out1 - clamp(lam, 0, 1) * out2.  Source: snap-research/TDA page
+    "triton_threshold_attention.py", ``differential_threshold_rela_triton``.
 ``nsa_ref(q, k, v, block_idx, block_size, rows=None)``
     NSA selection-branch forward (GQA softmax over the union of the selected
     blocks' causal tokens, scale D^-0.5), returning (out, lse).  Source:
@@ -65,6 +70,9 @@ def _load():
     lib.oracle_nsa_rows.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64, i64,
                                     i64, i64, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_nsa_rows.restype = ctypes.c_int
+    lib.oracle_tda_rows.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                                    dbl, dbl, dbl, ctypes.c_int, vp, i64, vp, ctypes.c_int]
+    lib.oracle_tda_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -125,6 +133,31 @@ def tra_ref(q, k, v, beta: float, p: float, rows=None, nthreads: int = 0) -> np.
                                  out.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_tra_rows rejected its arguments")
+    return out.reshape(B, H, T, D) if r is None else out
+
+
+def tda_ref(q1, q2, k1, k2, v, beta: float, lam: float, p: float, normalize: bool = True,
+            rows=None, nthreads: int = 0) -> np.ndarray:
+    """Threshold Differential Attention forward in fp64.
+
+    q1, q2, k1, k2, v: [B, H, T, D].  Returns float64 [B, H, T, D], or [len(rows), D].
+    """
+    arrs = [_as_input(x) for x in (q1, q2, k1, k2, v)]
+    dts = {a[1] for a in arrs}
+    if len(dts) != 1:
+        raise TypeError("q1, q2, k1, k2, v must share one dtype")
+    shapes = {a[0].shape for a in arrs}
+    if len(shapes) != 1 or arrs[0][0].ndim != 4:
+        raise ValueError("q1, q2, k1, k2, v must all be [B, H, T, D]")
+    B, H, T, D = arrs[0][0].shape
+    r, rp = _rows_arg(rows)
+    n = B * H * T if r is None else r.size
+    out = np.zeros((n, D), dtype=np.float64)
+    rc = _load().oracle_tda_rows(*(a[0].ctypes.data for a in arrs), dts.pop(),
+                                 B, H, T, D, float(beta), float(lam), float(p),
+                                 1 if normalize else 0, rp, n, out.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_tda_rows rejected its arguments")
     return out.reshape(B, H, T, D) if r is None else out
 
 

@@ -28,6 +28,13 @@
  *   (lse = max + log(sum) over the scaled scores, natural log, with the
  *   finite sentinel -1e9 for an empty row).
  *
+ * Threshold Differential Attention
+ *   source: snap-research/TDA, page "triton_threshold_attention.py",
+ *   `differential_threshold_rela_triton` (optionally L2-normalise q1, k1, q2,
+ *   k2 along the head dimension; two Threshold Rectified Attention outputs
+ *   over the same v, beta and p; combined as out1 - clamp(lambda, 0, 1)*out2)
+ *   and torch.nn.functional.normalize's definition x / max(||x||_2, 1e-12).
+ *
  * Threading: rows are independent; OpenMP spreads them over threads.  Each
  * row is computed by exactly one thread in a fixed order, so results do not
  * depend on the thread count.
@@ -211,6 +218,94 @@ int oracle_nsa_rows(const void *q, const void *k, const void *v, int dtype,
         }
         free(chosen);
         free(sc);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Row `row` (D values) of a [.., D] array, widened; with `normalize` divided by
+ * max(||row||_2, 1e-12) as torch.nn.functional.normalize(p=2, dim=-1) does. */
+static void load_row(const void *x, int dtype, int64_t row, int64_t D, int normalize,
+                     double *dst) {
+    double ss = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+        dst[d] = widen(x, dtype, row * D + d);
+        ss += dst[d] * dst[d];
+    }
+    if (!normalize) return;
+    double nrm = sqrt(ss);
+    if (nrm < 1e-12) nrm = 1e-12;
+    for (int64_t d = 0; d < D; ++d) dst[d] /= nrm;
+}
+
+/*
+ * Threshold Differential Attention forward for a list of output rows.
+ *
+ *   q1, q2, k1, k2, v : [B, H, T, D] dense row-major, fp32 or bf16 bits (dtype)
+ *   rows              : flat row ids r = (b*H + h)*T + i, or NULL for all rows
+ *   out               : [nrows, D] doubles
+ *
+ * With normalize != 0 every row of q1, q2, k1, k2 is first divided by
+ * max(||row||_2, 1e-12).  Then, the two paths taken one after the other as
+ * the page does,
+ *
+ *   out1 = sum_{j<=i} max(q1_i . k1_j - tau_i, 0)^p v_j
+ *   out2 = sum_{j<=i} max(q2_i . k2_j - tau_i, 0)^p v_j
+ *   out  = out1 - min(max(lambda, 0), 1) * out2,   tau_i = beta*sqrt(2 ln(i+1)/D)
+ *
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_tda_rows(const void *q1, const void *q2, const void *k1, const void *k2,
+                    const void *v, int dtype,
+                    int64_t B, int64_t H, int64_t T, int64_t D,
+                    double beta, double lambda, double p, int normalize,
+                    const int64_t *rows, int64_t nrows,
+                    double *out, int nthreads) {
+    if (!q1 || !q2 || !k1 || !k2 || !v || !out || B < 0 || H < 0 || T < 0 || D <= 0)
+        return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t total = B * H * T;
+    const double lam = lambda < 0.0 ? 0.0 : (lambda > 1.0 ? 1.0 : lambda);
+    if (!rows) nrows = total;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(6 * D));
+        if (!buf) bad = 1;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t n = 0; n < nrows; ++n) {
+            if (!buf) continue;
+            const int64_t r = rows ? rows[n] : n;
+            double *o = out + n * D;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            const int64_t bh = r / T, i = r % T;
+            double *qa = buf, *qb = buf + D, *ka = buf + 2 * D, *kb = buf + 3 * D;
+            double *o1 = buf + 4 * D, *o2 = buf + 5 * D;
+            load_row(q1, dtype, bh * T + i, D, normalize, qa);
+            load_row(q2, dtype, bh * T + i, D, normalize, qb);
+            const double tau = beta * sqrt(2.0 * log((double)(i + 1)) / (double)D);
+            for (int64_t d = 0; d < D; ++d) o1[d] = o2[d] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                load_row(k1, dtype, bh * T + j, D, normalize, ka);
+                load_row(k2, dtype, bh * T + j, D, normalize, kb);
+                double s1 = 0.0, s2 = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    s1 += qa[d] * ka[d];
+                    s2 += qb[d] * kb[d];
+                }
+                const double x1 = s1 - tau, x2 = s2 - tau;
+                const double w1 = x1 > 0.0 ? pow(x1, p) : 0.0;
+                const double w2 = x2 > 0.0 ? pow(x2, p) : 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    const double vd = widen(v, dtype, bh * T * D + j * D + d);
+                    o1[d] += w1 * vd;
+                    o2[d] += w2 * vd;
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) o[d] = o1[d] - lam * o2[d];
+        }
+        free(buf);
     }
     return bad ? -1 : 0;
 }
