@@ -222,8 +222,25 @@ int oracle_nsa_rows(const void *q, const void *k, const void *v, int dtype,
     return bad ? -1 : 0;
 }
 
+/* x rounded to the nearest value of the input dtype (ties to even): fp32, or
+ * bfloat16 (8 significant bits, fp32's exponent range). */
+static double round_to_dtype(double x, int dtype) {
+    if (dtype == ORACLE_F32) return (double)(float)x;
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    const double m = frexp(x, &e);              /* x = m * 2^e, 0.5 <= |m| < 1 */
+    if (e < -125) e = -125;                     /* below the normal range: fixed quantum */
+    const double q = ldexp(x, 8 - e);           /* 8 significant bits before the point */
+    const double r = nearbyint(q);              /* default rounding: to nearest, ties even */
+    (void)m;
+    return ldexp(r, e - 8);
+}
+
 /* Row `row` (D values) of a [.., D] array, widened; with `normalize` divided by
- * max(||row||_2, 1e-12) as torch.nn.functional.normalize(p=2, dim=-1) does. */
+ * max(||row||_2, 1e-12) as torch.nn.functional.normalize(p=2, dim=-1) does, and
+ * the quotient rounded back to the input dtype: the page normalises tensors of
+ * the input dtype and hands the normalised tensors, in that dtype, to the
+ * attention. */
 static void load_row(const void *x, int dtype, int64_t row, int64_t D, int normalize,
                      double *dst) {
     double ss = 0.0;
@@ -234,7 +251,7 @@ static void load_row(const void *x, int dtype, int64_t row, int64_t D, int norma
     if (!normalize) return;
     double nrm = sqrt(ss);
     if (nrm < 1e-12) nrm = 1e-12;
-    for (int64_t d = 0; d < D; ++d) dst[d] /= nrm;
+    for (int64_t d = 0; d < D; ++d) dst[d] = round_to_dtype(dst[d] / nrm, dtype);
 }
 
 /*
@@ -245,8 +262,9 @@ static void load_row(const void *x, int dtype, int64_t row, int64_t D, int norma
  *   out               : [nrows, D] doubles
  *
  * With normalize != 0 every row of q1, q2, k1, k2 is first divided by
- * max(||row||_2, 1e-12).  Then, the two paths taken one after the other as
- * the page does,
+ * max(||row||_2, 1e-12) and rounded back to the input dtype (bf16 or fp32,
+ * nearest-even), as the page's normalised tensors are.  Then, the two paths
+ * taken one after the other as the page does,
  *
  *   out1 = sum_{j<=i} max(q1_i . k1_j - tau_i, 0)^p v_j
  *   out2 = sum_{j<=i} max(q2_i . k2_j - tau_i, 0)^p v_j

@@ -28,15 +28,20 @@ def _five(B, H, T, D, seed):
     return [torch.randn(B, H, T, D, generator=g, dtype=torch.float32) for _ in range(5)]
 
 
-@pytest.mark.parametrize("mode", ["normalize", "raw"])
+@pytest.mark.parametrize("mode", ["normalize_bf16", "normalize_f32", "raw", "raw_bf16"])
 def test_tda_hand_example(mode):
-    """3-token example worked by hand (tests/golden/tda_hand_T3_D2.json)."""
+    """3-token example worked by hand (tests/golden/tda_hand_T3_D2.json).  With bf16
+    inputs the normalised rows are rounded to bf16 (exact fractions in the fixture);
+    with fp32 inputs to fp32, which moves the decimal hand values by ~1e-7."""
     with open(os.path.join(GOLDEN, "tda_hand_T3_D2.json")) as f:
         g = json.load(f)
-    q1, k1, q2, k2, v = (_f32(g[n])[None, None] for n in ("q1", "k1", "q2", "k2", "v"))
+    t = (lambda a: _f32(a).to(torch.bfloat16)) if mode.endswith("bf16") else _f32
+    q1, k1, q2, k2, v = (t(g[n])[None, None] for n in ("q1", "k1", "q2", "k2", "v"))
     out = oracle.tda_ref(q1, q2, k1, k2, v, g["beta"], g["lambda"], g["p"],
-                         normalize=(mode == "normalize"))[0, 0]
-    np.testing.assert_allclose(out, np.asarray(g["expected"][mode]), rtol=1e-12, atol=1e-12)
+                         normalize=mode.startswith("normalize"))[0, 0]
+    key = "raw" if mode.startswith("raw") else mode
+    rtol = 1e-6 if mode == "normalize_f32" else 1e-15
+    np.testing.assert_allclose(out, np.asarray(g["expected"][key]), rtol=rtol, atol=rtol)
 
 
 @pytest.mark.parametrize("beta,lam,p", [(-0.7, 0.3, 2.0), (-1.5, 1.0, 1.0), (-0.2, 0.75, 1.5)])
@@ -69,7 +74,7 @@ def test_tda_lambda_zero_is_tra_on_path_one():
             q1n = torch.nn.functional.normalize(q1.double(), dim=-1).float()
             k1n = torch.nn.functional.normalize(k1.double(), dim=-1).float()
             b = oracle.tra_ref(q1n, k1n, v, 0.4, 2.0)
-            np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)   # q1n, k1n rounded to fp32
+            assert np.array_equal(a, b)        # the normalised rows rounded to fp32 both ways
         else:
             assert np.array_equal(a, oracle.tra_ref(q1, k1, v, 0.4, 2.0))
 
@@ -141,7 +146,9 @@ def test_tda_brute_force_matrix_form(norm, p):
         x = x.double().numpy()
         if not norm:
             return x
-        return x / np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), 1e-12)
+        # normalised rows go back to the inputs' dtype (fp32 here; numpy rounds to nearest even)
+        y = x / np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), 1e-12)
+        return y.astype(np.float32).astype(np.float64)
     Q1, Q2, K1, K2 = nrm(q1), nrm(q2), nrm(k1), nrm(k2)
     V = v.double().numpy()
     tau = beta * np.sqrt(2.0 * np.log(np.arange(T) + 1.0) / D)[:, None]
@@ -159,3 +166,14 @@ def test_tda_rows_subset_matches_full():
     rows = np.array([0, 5, 21, 43, 10])
     part = oracle.tda_ref(q1, q2, k1, k2, v, 0.1, 0.5, 2.0, rows=rows)
     assert np.array_equal(part, full[rows])
+
+
+def test_tda_normalised_bf16_rows_match_an_independent_rounding():
+    """The oracle's bf16 rounding of normalised rows (nearest, ties to even) against
+    torch's own fp64 -> bf16 conversion, through lambda = 0 and beta = 0, p = 1 where
+    the output is a plain sum of the rounded cosines times v."""
+    q1, q2, k1, k2, v = inputs.tda_inputs(2, 2, 40, 64, seed=16)
+    a = oracle.tda_ref(q1, q2, k1, k2, v, 0.0, 0.0, 1.0, normalize=True)
+    rnd = lambda x: (x.double() / x.double().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    b = oracle.tra_ref(rnd(q1), rnd(k1), v, 0.0, 1.0)
+    assert np.array_equal(a, b)
