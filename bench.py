@@ -1,6 +1,6 @@
 """Benchmark of the fused causal-attention forwards on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
 
 One step is one pass over both forwards of the hot path, each on its own
 seeded synthetic batch already resident in HBM:
@@ -11,7 +11,11 @@ seeded synthetic batch already resident in HBM:
                  valid selected block per (b, kv head, query)).
 W untimed steps, then K timed steps between two device synchronisations.
 Per-launch kernel durations come from HIP events recorded on the stream the
-kernels run on.  Prints ONE JSON line.
+kernels run on.  After the timed steps, the other configurations of the method
+(TRA at T=2048 D=64 for p = 1, 2, 1.5; TRA fp32 at T=256; Threshold Differential
+Attention at T=8192 D=128; NSA G=8 at T=4096; NSA G=16 at T=32768 with caches
+flushed before each launch) are timed on their own
+and reported under "other_configs".  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -40,8 +44,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "causal_attention_tiled_amd", "csrc")
 # sources whose change invalidates a recorded traffic figure of each kernel
 KERNEL_SOURCES = {
-    "tra_fwd": ["tra_fwd.hip", "attn_internal.h"],
+    "tra_fwd": ["tra_fwd.hip", "attn_internal.h", "attn_tile.h"],
     "nsa_sel_fwd": ["nsa_sel_fwd.hip", "attn_internal.h"],
+    "tda_fwd": ["tda_fwd.hip", "attn_internal.h", "attn_tile.h"],
 }
 NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
 
@@ -139,6 +144,83 @@ def cpu_baseline_nsa(qn, kn, vn, idx_np, budget_s=8.0):
                       f"({spent:.1f} s), fp64; bytes counted per head"}
 
 
+def time_launches(fn, warm, timed, between=None):
+    """Per-launch durations (ms) of fn() from HIP events on the current stream;
+    between() (not timed) runs before every launch when given."""
+    for _ in range(warm):
+        if between is not None:
+            between()
+        fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(timed):
+        if between is not None:
+            between()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return ms
+
+
+def stats(ms):
+    return {"ms": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))}
+
+
+def extra_configs(dev, nsa_c5=None):
+    """The other workloads of the method at their own sizes (not the headline line):
+    TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
+    B2 H32 T8192 D128 (normalised); NSA G=8 at T=4096; and NSA G=16 at T=32768 with
+    L2 and MALL flushed before every launch."""
+    res = {}
+    B, H, T, D = 4, 16, 2048, 64
+    q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
+    out = torch.empty_like(q)
+    fl = tra_useful_flops(B, H, T, D)
+    for pw in (1.0, 2.0, 1.5):
+        st = stats(time_launches(lambda: cat.tra_fwd(q, k, v, 1.0, pw, out=out), 10, 20))
+        tf = fl / (st["ms"] * 1e-3) / 1e12
+        res[f"tra_fwd B4 H16 T2048 D64 p{pw:g}"] = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
+    q, k, v = (x.to(dev) for x in inputs.tra_inputs(1, 2, 256, 64, dtype=torch.float32, seed=0))
+    out = torch.empty_like(q)
+    res["tra_fwd_f32 B1 H2 T256 D64 p2"] = stats(
+        time_launches(lambda: cat.tra_fwd_f32(q, k, v, 1.0, 2.0, out=out), 10, 20))
+    c = inputs.CONFIGS["tda_bf16_T8192_D128"]
+    B, H, T, D = c["B"], c["H"], c["T"], c["D"]
+    t5 = [x.to(dev) for x in inputs.tda_inputs(B, H, T, D, seed=0)]
+    ws = torch.empty(cat.tda_workspace_bytes(B, H, T, D, c["normalize"]), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(t5[0])
+    fl = 6.0 * D * B * H * T * (T + 1) / 2.0      # two score products and one weighted sum per pair
+    st = stats(time_launches(lambda: cat.tda_fwd(*t5, c["beta"], c["lam"], 2.0,
+                                                 normalize=c["normalize"], out=out, workspace=ws),
+                             10, 20))
+    tf = fl / (st["ms"] * 1e-3) / 1e12
+    res["tda_fwd B2 H32 T8192 D128 normalised beta=D^-1/2 lambda=0.5 p2 (6D FLOP per pair)"] = dict(
+        st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
+    del t5, ws, out
+    B, Hq, Hkv, T, D, bs, S = 2, 32, 4, 4096, 128, 64, 16
+    qn, kn, vn = (x.to(dev) for x in inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0))
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
+    gidx = torch.from_numpy(idx).to(dev)
+    o = torch.empty_like(qn)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    gb = nsa_gathered_bytes(idx, T, bs, D)
+    st = stats(time_launches(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), 10, 20))
+    res["nsa_sel_fwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"] = dict(
+        st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
+    if nsa_c5 is not None:
+        fn, gb = nsa_c5
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        st = stats(time_launches(fn, 2, 8, between=lambda: flush.fill_(1)))
+        res["nsa_sel_fwd B1 Hq64 Hkv4 T32768 D128 bs64 S16, cold (512 MiB written before each launch)"] = dict(
+            st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
+        del flush
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +232,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run a plain device copy of this many bytes (3 times), the "
                          "reference for calibrating HBM traffic counters")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the timings of the other configurations")
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each kernel and exit")
     args = ap.parse_args()
@@ -256,13 +340,20 @@ def main():
         "config": {"workload": "tra_fwd B2 H32 T8192 D128 beta1 p2 + nsa_sel_fwd B1 Hq64 Hkv4 "
                                "T32768 D128 bs64 S16",
                    "tra": TRA, "nsa": NSA},
-        "tra_fwd": {"ms": tra_avg, "tflops": tra_tflops,
+        "tra_fwd": {"ms": tra_avg, "ms_median": float(np.median(tra_ms)),
+                    "ms_min": float(np.min(tra_ms)), "tflops": tra_tflops,
                     "frac_bf16_peak": tra_tflops / PEAK_BF16_TFLOPS},
-        "nsa_sel_fwd": {"ms": nsa_avg, "gathered_gb": gbytes / 1e9, "gbps": nsa_gbps,
-                        "frac_hbm_peak": nsa_gbps / PEAK_HBM_GBPS},
+        "nsa_sel_fwd": {"ms": nsa_avg, "ms_median": float(np.median(nsa_ms)),
+                        "ms_min": float(np.min(nsa_ms)), "gathered_gb": gbytes / 1e9,
+                        "gbps": nsa_gbps, "frac_hbm_peak": nsa_gbps / PEAK_HBM_GBPS},
         "roofline": dominant,
         "roofline_all": {"tra_fwd": roof_tra, "nsa_sel_fwd": roof_nsa},
     }
+    if not args.no_extra and args.only is None:
+        print("bench: other configurations", file=sys.stderr, flush=True)
+        c5 = (lambda: cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n),
+              gbytes)
+        result["other_configs"] = extra_configs(dev, nsa_c5=c5)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(q, k, v, idx_np)

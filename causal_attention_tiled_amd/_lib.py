@@ -43,6 +43,11 @@ def load_library():
     lib.tra_fwd.restype = ci
     lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_fwd_f32.restype = ci
+    lib.tda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                            ci, ci, ci, ci, cf, cf, cf, ci, vp]
+    lib.tda_fwd.restype = ci
+    lib.tda_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.tda_workspace_bytes.restype = ctypes.c_size_t
     lib.nsa_sel_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
     lib.nsa_sel_fwd.restype = ci
     lib.attn_status_str.argtypes = [ci]
@@ -102,6 +107,45 @@ def tra_fwd(q, k, v, beta, p, out=None, stream=None):
 def tra_fwd_f32(q, k, v, beta, p, out=None, stream=None):
     """Threshold Rectified Attention forward, fp32 in / fp32 out."""
     return _tra("tra_fwd_f32", torch.float32, q, k, v, beta, p, out, stream)
+
+
+def tda_workspace_bytes(B, H, T, D, normalize=True) -> int:
+    """Bytes of device workspace tda_fwd needs (0 without normalisation)."""
+    return int(load_library().tda_workspace_bytes(B, H, T, D, 1 if normalize else 0))
+
+
+def tda_fwd(q1, q2, k1, k2, v, beta, lam, p, normalize=True, out=None, workspace=None,
+            stream=None):
+    """Threshold Differential Attention forward, bf16 in / bf16 out.
+
+    q1, q2, k1, k2, v: contiguous bfloat16 [B, H, T, D] on the GPU.  ``workspace``
+    (uint8 GPU tensor of at least ``tda_workspace_bytes`` bytes) is allocated here
+    when not given and normalisation needs it.  Returns ``out``.
+    """
+    for t, n in ((q1, "q1"), (q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    if q1.dim() != 4 or any(t.shape != q1.shape for t in (q2, k1, k2, v)):
+        raise ValueError("q1, q2, k1, k2, v must all be [B, H, T, D]")
+    if out is None:
+        out = torch.empty_like(q1)
+    _check(out, "out", torch.bfloat16)
+    if out.shape != q1.shape:
+        raise ValueError("out must match q1's shape")
+    B, H, T, D = q1.shape
+    need = tda_workspace_bytes(B, H, T, D, normalize)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q1.device)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace", workspace.dtype)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = load_library().tda_fwd(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(), k2.data_ptr(),
+                                v.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes, B, H, T, D,
+                                float(beta), float(lam), float(p), 1 if normalize else 0,
+                                _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("tda_fwd", rc)
+    return out
 
 
 def nsa_sel_fwd(q, k, v, block_idx, block_size, out=None, lse=None, stream=None,

@@ -29,12 +29,12 @@ CXXFLAGS = [
 ]
 
 
-# Per-file extra flags.  Threshold Rectified Attention: inputs are finite by
+# Per-file extra flags.  Threshold attention kernels: inputs are finite by
 # contract, so max(x, 0) needs no NaN canonicalisation; MFMA results go to the
 # vector registers the epilogue reads (the allocator then keeps the loop-invariant
 # Q operands in the accumulation registers instead).
-EXTRA = {"tra_fwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee",
-                         "-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+_THRESHOLD_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+EXTRA = {"tra_fwd.hip": _THRESHOLD_FLAGS, "tda_fwd.hip": _THRESHOLD_FLAGS}
 
 
 def _hipcc() -> str:

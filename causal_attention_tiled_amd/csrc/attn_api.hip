@@ -58,6 +58,35 @@ ATTN_EXPORT int tra_fwd_f32(const float *q, const float *k, const float *v, floa
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+ATTN_EXPORT size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize) {
+    if (!normalize || B <= 0 || H <= 0 || T <= 0 || D <= 0) return 0;
+    return (size_t)2 * (size_t)B * (size_t)H * (size_t)T * (size_t)D * 2;
+}
+
+ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const void *k2,
+                        const void *v, void *out, void *workspace, size_t workspace_bytes,
+                        int B, int H, int T, int D, float beta, float lambda, float p,
+                        int normalize, void *stream) {
+    if (!isfinite(lambda)) return ATTN_ERR_SHAPE;
+    bool noop;
+    const int st = tra_validate(q1, k1, v, out, B, H, T, D, beta, p, attn::kTdaRows, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if (!q2 || !k2) return ATTN_ERR_NULL;
+    if (misaligned(q2) || misaligned(k2)) return ATTN_ERR_ALIGN;
+    const size_t need = tda_workspace_bytes(B, H, T, D, normalize);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    }
+    const hipError_t e = attn::launch_tda_fwd_bf16(
+        static_cast<const uint16_t *>(q1), static_cast<const uint16_t *>(q2),
+        static_cast<const uint16_t *>(k1), static_cast<const uint16_t *>(k2),
+        static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out),
+        static_cast<uint16_t *>(workspace), B * H, T, D, beta, lambda, p, normalize ? 1 : 0,
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
                             const int32_t *block_idx, void *out, float *lse, int B, int Hq,
                             int Hkv, int T, int D, int block_size, int S, void *stream) {
@@ -90,6 +119,7 @@ ATTN_EXPORT const char *attn_status_str(int status) {
         case ATTN_ERR_UNSUPPORTED: return "unsupported head dim, block size or group size";
         case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         default: return "unknown status";
     }
 }

@@ -47,6 +47,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Query rows per workgroup of the bf16 / fp32 Threshold Rectified Attention kernels.
 constexpr int kTraBf16Rows = 256;
 constexpr int kTraF32Rows = 64;
+// Query rows per workgroup of the Threshold Differential Attention kernel.
+constexpr int kTdaRows = 256;
 
 // Host-side launchers (one per kernel family); they pick the template
 // instance and return the HIP launch status.
@@ -55,6 +57,10 @@ hipError_t launch_tra_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                hipStream_t stream);
 hipError_t launch_tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
                               int BH, int T, int D, float beta, float p, hipStream_t stream);
+hipError_t launch_tda_fwd_bf16(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,
+                               const uint16_t *k2, const uint16_t *v, uint16_t *out,
+                               uint16_t *workspace, int BH, int T, int D, float beta,
+                               float lam, float p, int normalize, hipStream_t stream);
 hipError_t launch_nsa_sel_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const int32_t *block_idx, uint16_t *out, float *lse, int B,
                               int Hq, int Hkv, int T, int D, int block_size, int S,

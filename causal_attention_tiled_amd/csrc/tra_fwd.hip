@@ -5,28 +5,29 @@
 //     out_i = sum_{j <= i} max(q_i . k_j - tau_i, 0)^p v_j,   tau_i = beta*sqrt(2 ln(i+1) / D)
 // with a 0-based query position i, natural log, no 1/sqrt(D) scale and no softmax.
 //
-// bf16 kernel design (one workgroup = 4 wavefronts = 128 query rows of one (b,h)):
+// bf16 kernel design (one workgroup = 8 wavefronts = 256 query rows of one (b,h),
+// two wavefronts per SIMD):
 //  * Each wave owns 32 query rows.  It computes the TRANSPOSED score tile
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, K (A operand) from LDS, Q (B operand)
 //    held in registers for the whole key loop.  In the accumulator every lane then
-//    holds ONE query (lane % 32) and 16 keys, so tau_i is a per-lane scalar and the
-//    causal test is a per-lane compare.
-//  * The epilogue (threshold, ReLU, power, causal mask) runs on those registers and
-//    rounds the weights to bf16; the register order of the accumulator directly forms
-//    the B operand of O^T += V^T P^T (again 32x32x16), so P never touches LDS.  The
-//    key order this implies is absorbed into the V^T layout in LDS.
-//  * K and V tiles of 64 keys are double-buffered through LDS: the next tile's global
-//    loads are issued before the current tile's MFMAs and written to the other buffer
-//    afterwards (one barrier per tile).  V is transposed on its way into LDS.
+//    holds ONE query (lane % 32) and 16 keys, so tau_i is a per-lane scalar (folded
+//    into the accumulator's initial value) and the causal test is a per-lane compare.
+//  * The epilogue (ReLU, power, causal mask) runs on those registers and rounds the
+//    weights to bf16; the register order of the accumulator directly forms the B
+//    operand of O^T += V^T P^T (again 32x32x16), so P never touches LDS.  V stays
+//    row-major in LDS and is read as the V^T operand with transposing LDS reads.
+//  * K and V tiles of 64 keys go from HBM straight into LDS (buffer loads with the
+//    LDS as destination), double-buffered: the next tile's loads are issued at the
+//    start of the current tile and awaited, with one barrier, at its end.
 //  * Causal tile skipping: key tiles past the workgroup's last query are never loaded;
-//    32-key sub-tiles past a wave's last query are skipped by that wave; the mask is
-//    evaluated only on sub-tiles that straddle the diagonal.
+//    tiles wholly after a wave's rows are skipped by that wave; the mask is evaluated
+//    only on tiles that reach past a wave's first row.
 //  * Launch order: the heaviest query tiles (largest i) first, and the heads split
 //    into 8 contiguous groups so that each XCD (dispatch is round-robin over the 8
 //    XCDs) works on its own heads and keeps their K/V in its private L2.
 #include <type_traits>
 
-#include "attn_internal.h"
+#include "attn_tile.h"
 
 namespace attn {
 namespace {
@@ -36,76 +37,6 @@ constexpr int kQueryBlocks = 1;  // bf16 kernel: 32-row query blocks per wave
 constexpr int kWaves = 8;        // bf16 kernel: wavefronts per workgroup
 static_assert(kWaves * 32 * kQueryBlocks == kTraBf16Rows, "workgroup rows");
 constexpr int kBN = 64;   // keys per LDS tile
-
-enum PowMode { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2 };
-
-template <int PM>
-__device__ __forceinline__ float relu_pow(float x, float p) {
-    if constexpr (PM == kPowOne) {
-        return fmaxf(x, 0.0f);
-    } else if constexpr (PM == kPowTwo) {
-        const float r = fmaxf(x, 0.0f);
-        return r * r;
-    } else {
-        // x^p = 2^(p log2 x) for x > 0 (v_log_f32 / v_exp_f32 are base 2).
-        return x > 0.0f ? __builtin_amdgcn_exp2f(p * __builtin_amdgcn_logf(x)) : 0.0f;
-    }
-}
-
-// Workgroup id -> (head slab, query tile).  Heavy tiles first; with BH % 8 == 0
-// the heads are split into 8 contiguous ranges, one per XCD (workgroup ids are
-// dealt to XCDs round-robin, so id % 8 names the XCD).
-__device__ __forceinline__ void tra_tile_of(int bid, int BH, int nqt, int &bh, int &qt) {
-    if ((BH & 7) == 0) {
-        const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
-        bh = xcd * hpx + s % hpx;
-        qt = nqt - 1 - s / hpx;
-    } else {
-        bh = bid % BH;
-        qt = nqt - 1 - bid / BH;
-    }
-}
-
-// LDS tile layout (K and V alike): row-major [key][dim], D*2 bytes per row, no
-// padding; the 16-byte chunk c of row r sits in chunk slot c ^ tile_swz<D>(r).  The
-// LDS has 64 four-byte banks (256 bytes per cycle).  With this swizzle the 16 rows
-// that 16 consecutive lanes read for the K operand (ds_read_b128), and the 4 rows x
-// 64 bytes that 32 lanes read for the V operand (ds_read_b64_tr_b16), each cover
-// all 64 banks once.
-template <int D>
-__device__ __forceinline__ int tile_swz(int row) {
-    if constexpr (D == 128)  // one row per bank line, 16 chunk slots
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    else                     // two 128-byte rows per bank line, 8 chunk slots
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-
-// Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`, held in scalar
-// registers; loads past the end return 0.
-__device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
-               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu), bytes,
-               0x00020000u};
-    return r;
-}
-
-// 16 bytes per lane from global memory (resource + voff + soff) straight into LDS at
-// lds + 16 * lane.  Issued as inline assembly so that the compiler does not add its
-// own (conservative) waits for it before unrelated LDS reads: completion is awaited
-// explicitly, with s_waitcnt vmcnt, before the barrier that publishes the tile.
-// M0 carries the LDS address and is set here for each transfer.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(u32x4 rsrc, void *lds, int voff, int soff) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 template <int D, int PM, int QB, int NW>
 __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
@@ -130,7 +61,7 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     typedef uint8_t TileBuf[2][TILEB];
 
     int bh, qt;
-    tra_tile_of(blockIdx.x, BH, nqt, bh, qt);
+    tile_order(blockIdx.x, BH, nqt, bh, qt);
     // workgroup-uniform: keep them (and the buffer resources built from them) scalar
     bh = __builtin_amdgcn_readfirstlane(bh);
     qt = __builtin_amdgcn_readfirstlane(qt);

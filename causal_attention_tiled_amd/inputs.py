@@ -34,6 +34,19 @@ def tra_inputs(B: int, H: int, T: int, D: int, dtype=torch.bfloat16, seed: int =
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
+def tda_inputs(B: int, H: int, T: int, D: int, dtype=torch.bfloat16, seed: int = 0):
+    """q1, q2, k1, k2, v [B, H, T, D] on the CPU: q and k rows N(0, D^-1/2) (so raw
+    scores are about N(0, 1)), v N(0, 1); drawn in that order."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    std_qk = float(D) ** -0.25
+    q1 = _draw((B, H, T, D), std_qk, gen)
+    q2 = _draw((B, H, T, D), std_qk, gen)
+    k1 = _draw((B, H, T, D), std_qk, gen)
+    k2 = _draw((B, H, T, D), std_qk, gen)
+    v = _draw((B, H, T, D), 1.0, gen)
+    return tuple(t.to(dtype) for t in (q1, q2, k1, k2, v))
+
+
 def nsa_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype=torch.bfloat16, seed: int = 0):
     """q [B, Hq, T, D], k, v [B, Hkv, T, D] on the CPU, N(0, 1), in ``dtype``."""
     gen = torch.Generator(device="cpu").manual_seed(seed)
@@ -71,13 +84,18 @@ def nsa_block_idx(B: int, Hkv: int, T: int, block_size: int, S: int, seed: int =
     return out.reshape(B, Hkv, T, S)
 
 
-# The five workloads the library is measured and checked on.
+# The workloads the library is measured and checked on.
 CONFIGS = {
     "tra_f32_T256": dict(kind="tra", dtype="f32", B=1, H=2, T=256, D=64, beta=1.0, p=[2.0]),
     "tra_bf16_T2048_D64": dict(kind="tra", dtype="bf16", B=4, H=16, T=2048, D=64, beta=1.0,
                                p=[1.0, 2.0, 1.5]),
     "tra_bf16_T8192_D128": dict(kind="tra", dtype="bf16", B=2, H=32, T=8192, D=128, beta=1.0,
                                 p=[2.0]),
+    # Threshold Differential Attention at the T=8192 D=128 shape, normalised rows;
+    # beta = D^-1/2 puts the thresholds at the same multiple of the cosines' spread
+    # (D^-1/2) as beta = 1 does for the raw scores above.
+    "tda_bf16_T8192_D128": dict(kind="tda", dtype="bf16", B=2, H=32, T=8192, D=128,
+                                beta=128 ** -0.5, lam=0.5, p=[2.0], normalize=True),
     "nsa_bf16_T4096_G8": dict(kind="nsa", dtype="bf16", B=2, Hq=32, Hkv=4, T=4096, D=128,
                               block_size=64, S=16),
     "nsa_bf16_T32768_G16": dict(kind="nsa", dtype="bf16", B=1, Hq=64, Hkv=4, T=32768, D=128,

@@ -25,6 +25,7 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -37,6 +38,7 @@ extern "C" {
 #define ATTN_ERR_UNSUPPORTED (-3) /* valid but not built: head dim, block size, group size */
 #define ATTN_ERR_ALIGN (-4)       /* a tensor pointer is not 16-byte aligned */
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
+#define ATTN_ERR_WORKSPACE (-6)   /* workspace missing or smaller than required */
 
 /*
  * Threshold Rectified Attention forward, bf16 in / bf16 out.
@@ -74,6 +76,45 @@ int tra_fwd(const void *q, const void *k, const void *v, void *out,
  */
 int tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
                 int B, int H, int T, int D, float beta, float p, void *stream);
+
+/*
+ * Threshold Differential Attention forward, bf16 in / bf16 out.
+ *
+ * Source: snap-research/TDA, page "triton_threshold_attention.py" --
+ * `differential_threshold_rela_triton` (optional L2 normalisation of q1, k1,
+ * q2, k2 along the head dimension, two Threshold Rectified Attention outputs
+ * over the same v, beta and p, combined as out1 - clamp(lambda, 0, 1) * out2),
+ * with torch.nn.functional.normalize's x / max(||x||_2, 1e-12).
+ *
+ *   out[b,h,i,:] = sum_{j<=i} ( max(a1_ij - tau_i, 0)^p
+ *                               - lam * max(a2_ij - tau_i, 0)^p ) * v_j
+ *   a_ij = q_i . k_j (normalize == 0) or the cosine of q_i and k_j (normalize != 0)
+ *   lam  = min(max(lambda, 0), 1),   tau_i = beta * sqrt(2 * ln(i + 1) / D)
+ *
+ *   q1, q2, k1, k2, v : bf16 [B, H, T, D]      (read only)
+ *   out               : bf16 [B, H, T, D]      (written; may not alias an input)
+ *   workspace         : device memory the call may overwrite, at least
+ *                       tda_workspace_bytes(B, H, T, D, normalize) bytes, 16-byte
+ *                       aligned; it holds the normalised k1 and k2 rows.  May be
+ *                       NULL when that size is 0 (normalize == 0).  Smaller or
+ *                       NULL when needed: ATTN_ERR_WORKSPACE.  Calls that share
+ *                       one workspace must not overlap in time.
+ *   D                 : 64 or 128 (else ATTN_ERR_UNSUPPORTED)
+ *   beta, lambda      : finite (else ATTN_ERR_SHAPE)
+ *   p                 : finite and > 0 (else ATTN_ERR_SHAPE)
+ *
+ * Numerics: as tra_fwd; normalised rows are rounded to bf16; the two
+ * weights of a pair are combined in fp32 and rounded to bf16 once, and one
+ * fp32 accumulation over v gives the output (rounded to bf16 once).
+ */
+int tda_fwd(const void *q1, const void *q2, const void *k1, const void *k2, const void *v,
+            void *out, void *workspace, size_t workspace_bytes,
+            int B, int H, int T, int D, float beta, float lambda, float p, int normalize,
+            void *stream);
+
+/* Workspace bytes tda_fwd needs for these sizes (0 when normalize == 0, or
+ * when a size is negative or zero). */
+size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize);
 
 /*
  * NSA selection-branch forward, bf16 in / bf16 out, fp32 lse.

@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN = 0, -1, -2, -3, -4
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK = 0, -1, -2, -3, -4, -5, -6
 P = 0x10000  # a 16-byte aligned dummy address (never touched by validation)
 
 
@@ -31,7 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("tra_fwd", "tra_fwd_f32", "nsa_sel_fwd", "attn_status_str"):
+    for n in ("tra_fwd", "tra_fwd_f32", "tda_fwd", "tda_workspace_bytes", "nsa_sel_fwd",
+              "attn_status_str"):
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     import causal_attention_tiled_amd as cat
-    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, -5):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK):
         assert cat.attn_status_str(code) not in ("", "unknown status")
     assert cat.attn_status_str(12345) == "unknown status"
 
@@ -93,6 +94,31 @@ def test_nsa_validation(lib):
     assert _nsa(lib, lse=P + 1) == EALIGN
     assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, T=0) == OK
     assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, B=0) == OK
+
+
+def _tda(lib, q1=P, q2=P, k1=P, k2=P, v=P, o=P, ws=P, ws_bytes=1 << 40, B=1, H=1, T=8, D=128,
+         beta=0.1, lam=0.5, p=2.0, norm=1):
+    return lib.tda_fwd(q1, q2, k1, k2, v, o, ws, ws_bytes, B, H, T, D, beta, lam, p, norm, None)
+
+
+def test_tda_validation(lib):
+    assert lib.tda_workspace_bytes(2, 3, 5, 128, 1) == 2 * 2 * 3 * 5 * 128 * 2
+    assert lib.tda_workspace_bytes(2, 3, 5, 128, 0) == 0
+    assert lib.tda_workspace_bytes(-1, 3, 5, 128, 1) == 0
+    assert _tda(lib, q2=None) == ENULL
+    assert _tda(lib, k1=None) == ENULL
+    assert _tda(lib, o=None) == ENULL
+    assert _tda(lib, T=-1) == ESHAPE
+    assert _tda(lib, lam=float("nan")) == ESHAPE
+    assert _tda(lib, beta=float("inf")) == ESHAPE
+    assert _tda(lib, p=-1.0) == ESHAPE
+    assert _tda(lib, D=96) == EUNSUP
+    assert _tda(lib, k2=P + 8) == EALIGN
+    assert _tda(lib, ws=None) == EWORK
+    assert _tda(lib, ws_bytes=2 * 8 * 128 * 2 - 1) == EWORK
+    assert _tda(lib, ws=P + 4) == EALIGN
+    # no normalisation needs no workspace; an empty problem is a no-op
+    assert _tda(lib, q1=None, q2=None, k1=None, k2=None, v=None, o=None, ws=None, T=0) == OK
 
 
 def test_binding_refuses_cpu_tensors(lib):
