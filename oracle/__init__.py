@@ -10,6 +10,10 @@ Functions
     Threshold Rectified Attention, out_i = sum_{j<=i} ReLU(q_i.k_j - tau_i)^p v_j,
     tau_i = beta*sqrt(2 ln(i+1)/D).  Source: snap-research/TDA page
     "triton_threshold_attention.py", module docstring and the forward kernel.
+``tra_bwd_ref(q, k, v, dout, beta, p, qrows=None, krows=None)``
+    Threshold Rectified Attention backward: (dq, dk, dv) in fp64 for the given
+    query rows (dq) and key rows (dk, dv).  Source: the same page's backward
+    kernels and autograd function (gradients of q, k, v).
 ``tda_ref(q1, q2, k1, k2, v, beta, lam, p, normalize=True, rows=None)``
     Threshold Differential Attention: optional L2 normalisation of the q and k
     rows, two Threshold Rectified Attention outputs over the same v, combined
@@ -73,6 +77,9 @@ def _load():
     lib.oracle_tda_rows.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
                                     dbl, dbl, dbl, ctypes.c_int, vp, i64, vp, ctypes.c_int]
     lib.oracle_tda_rows.restype = ctypes.c_int
+    lib.oracle_tra_bwd_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dbl,
+                                        dbl, vp, i64, vp, vp, i64, vp, vp, ctypes.c_int]
+    lib.oracle_tra_bwd_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -134,6 +141,36 @@ def tra_ref(q, k, v, beta: float, p: float, rows=None, nthreads: int = 0) -> np.
     if rc != 0:
         raise ValueError("oracle_tra_rows rejected its arguments")
     return out.reshape(B, H, T, D) if r is None else out
+
+
+def tra_bwd_ref(q, k, v, dout, beta: float, p: float, qrows=None, krows=None,
+                nthreads: int = 0):
+    """Threshold Rectified Attention backward in fp64.
+
+    q, k, v, dout: [B, H, T, D].  Returns (dq, dk, dv) as float64 [B, H, T, D] each, or,
+    when qrows / krows are given, dq as [len(qrows), D] and dk, dv as [len(krows), D].
+    """
+    arrs = [_as_input(x) for x in (q, k, v, dout)]
+    if len({a[1] for a in arrs}) != 1:
+        raise TypeError("q, k, v, dout must share one dtype")
+    if len({a[0].shape for a in arrs}) != 1 or arrs[0][0].ndim != 4:
+        raise ValueError("q, k, v, dout must all be [B, H, T, D]")
+    B, H, T, D = arrs[0][0].shape
+    qr, qp = _rows_arg(qrows)
+    kr, kp = _rows_arg(krows)
+    nq = B * H * T if qr is None else qr.size
+    nk = B * H * T if kr is None else kr.size
+    dq = np.zeros((nq, D), dtype=np.float64)
+    dk = np.zeros((nk, D), dtype=np.float64)
+    dv = np.zeros((nk, D), dtype=np.float64)
+    rc = _load().oracle_tra_bwd_rows(*(a[0].ctypes.data for a in arrs), arrs[0][1], B, H, T, D,
+                                     float(beta), float(p), qp, nq, dq.ctypes.data, kp, nk,
+                                     dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_tra_bwd_rows rejected its arguments")
+    shape = (B, H, T, D)
+    return (dq.reshape(shape) if qr is None else dq, dk.reshape(shape) if kr is None else dk,
+            dv.reshape(shape) if kr is None else dv)
 
 
 def tda_ref(q1, q2, k1, k2, v, beta: float, lam: float, p: float, normalize: bool = True,

@@ -28,6 +28,12 @@
  *   (lse = max + log(sum) over the scaled scores, natural log, with the
  *   finite sentinel -1e9 for an empty row).
  *
+ * Threshold Rectified Attention backward
+ *   source: the same page, `_threshold_rela_bwd_kernel_dq`,
+ *   `_threshold_rela_bwd_kernel_dkv` and `ThresholdRelaFunction.backward`
+ *   (gradients of q, k and v only; with x = q_i.k_j - tau_i the weight's
+ *   derivative is p * max(x, 0)^(p-1) for x > 0 and 0 otherwise).
+ *
  * Threshold Differential Attention
  *   source: snap-research/TDA, page "triton_threshold_attention.py",
  *   `differential_threshold_rela_triton` (optionally L2-normalise q1, k1, q2,
@@ -324,6 +330,87 @@ int oracle_tda_rows(const void *q1, const void *q2, const void *k1, const void *
             for (int64_t d = 0; d < D; ++d) o[d] = o1[d] - lam * o2[d];
         }
         free(buf);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Threshold Rectified Attention backward, for a list of query rows (dq) and a
+ * list of key rows (dk, dv).
+ *
+ *   q, k, v, dout : [B, H, T, D] dense row-major, fp32 or bf16 bits (dtype)
+ *   qrows, nq     : flat query-row ids (b*H + h)*T + i, or NULL for all rows
+ *   dq            : [nq, D] doubles (may be NULL to skip)
+ *   krows, nk     : flat key-row ids (b*H + h)*T + j, or NULL for all rows
+ *   dk, dv        : [nk, D] doubles (each may be NULL to skip)
+ *
+ * With x_ij = q_i . k_j - tau_i (tau_i = beta*sqrt(2 ln(i+1)/D)) and, for the
+ * causal pairs j <= i with x_ij > 0,
+ *   w_ij = x_ij^p,   g_ij = p * x_ij^(p-1),   a_ij = (dout_i . v_j) * g_ij
+ * (pairs with x_ij <= 0 or j > i have w = a = 0):
+ *   dq_i = sum_{j<=i} a_ij k_j,   dk_j = sum_{i>=j} a_ij q_i,   dv_j = sum_{i>=j} w_ij dout_i
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_tra_bwd_rows(const void *q, const void *k, const void *v, const void *dout,
+                        int dtype, int64_t B, int64_t H, int64_t T, int64_t D,
+                        double beta, double p,
+                        const int64_t *qrows, int64_t nq, double *dq,
+                        const int64_t *krows, int64_t nk, double *dk, double *dv,
+                        int nthreads) {
+    if (!q || !k || !v || !dout || B < 0 || H < 0 || T < 0 || D <= 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t total = B * H * T;
+    if (!qrows) nq = total;
+    if (!krows) nk = total;
+    set_threads(nthreads);
+    int bad = 0;
+    if (dq) {
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+        for (int64_t n = 0; n < nq; ++n) {
+            const int64_t r = qrows ? qrows[n] : n;
+            double *o = dq + n * D;
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            const int64_t bh = r / T, i = r % T, head = bh * T * D;
+            const double tau = beta * sqrt(2.0 * log((double)(i + 1)) / (double)D);
+            for (int64_t j = 0; j <= i; ++j) {
+                double s = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    s += widen(q, dtype, head + i * D + d) * widen(k, dtype, head + j * D + d);
+                    dp += widen(dout, dtype, head + i * D + d) * widen(v, dtype, head + j * D + d);
+                }
+                const double x = s - tau;
+                if (!(x > 0.0)) continue;
+                const double a = dp * p * pow(x, p - 1.0);
+                for (int64_t d = 0; d < D; ++d) o[d] += a * widen(k, dtype, head + j * D + d);
+            }
+        }
+    }
+    if (dk || dv) {
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+        for (int64_t n = 0; n < nk; ++n) {
+            const int64_t r = krows ? krows[n] : n;
+            if (dk) for (int64_t d = 0; d < D; ++d) dk[n * D + d] = 0.0;
+            if (dv) for (int64_t d = 0; d < D; ++d) dv[n * D + d] = 0.0;
+            if (r < 0 || r >= total) { bad = 1; continue; }
+            const int64_t bh = r / T, j = r % T, head = bh * T * D;
+            for (int64_t i = j; i < T; ++i) {
+                const double tau = beta * sqrt(2.0 * log((double)(i + 1)) / (double)D);
+                double s = 0.0, dp = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    s += widen(q, dtype, head + i * D + d) * widen(k, dtype, head + j * D + d);
+                    dp += widen(dout, dtype, head + i * D + d) * widen(v, dtype, head + j * D + d);
+                }
+                const double x = s - tau;
+                if (!(x > 0.0)) continue;
+                const double w = pow(x, p);
+                const double a = dp * p * pow(x, p - 1.0);
+                for (int64_t d = 0; d < D; ++d) {
+                    if (dk) dk[n * D + d] += a * widen(q, dtype, head + i * D + d);
+                    if (dv) dv[n * D + d] += w * widen(dout, dtype, head + i * D + d);
+                }
+            }
+        }
     }
     return bad ? -1 : 0;
 }
