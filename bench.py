@@ -13,8 +13,9 @@ W untimed steps, then K timed steps between two device synchronisations.
 Per-launch kernel durations come from HIP events recorded on the stream the
 kernels run on.  After the timed steps, the other configurations of the method
 (TRA at T=2048 D=64 for p = 1, 2, 1.5; TRA fp32 at T=256; Threshold Differential
-Attention at T=8192 D=128; NSA G=8 at T=4096; NSA G=16 at T=32768 with caches
-flushed before each launch) are timed on their own
+Attention at T=8192 D=128; the TRA backward at T=8192 D=128; NSA G=8 at T=4096;
+NSA G=16 at T=32768 with caches flushed before each launch) are timed on their
+own
 and reported under "other_configs".  Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -47,6 +48,7 @@ KERNEL_SOURCES = {
     "tra_fwd": ["tra_fwd.hip", "attn_internal.h", "attn_tile.h"],
     "nsa_sel_fwd": ["nsa_sel_fwd.hip", "attn_internal.h"],
     "tda_fwd": ["tda_fwd.hip", "attn_internal.h", "attn_tile.h"],
+    "tra_bwd": ["tra_bwd.hip", "attn_internal.h", "attn_tile.h"],
 }
 NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
 
@@ -169,24 +171,45 @@ def stats(ms):
     return {"ms": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms))}
 
 
+def batch_ms(fn, n):
+    """Mean duration of n back-to-back launches between two events (launch latency
+    overlapped, as in a stream of work)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def timed(fn, warm=10, per_launch=20, batch=50):
+    """Per-launch statistics, with "ms" the mean of a back-to-back batch."""
+    st = stats(time_launches(fn, warm, per_launch))
+    st["ms_per_launch_mean"] = st["ms"]
+    st["ms"] = batch_ms(fn, batch)
+    return st
+
+
 def extra_configs(dev, nsa_c5=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
-    B2 H32 T8192 D128 (normalised); NSA G=8 at T=4096; and NSA G=16 at T=32768 with
-    L2 and MALL flushed before every launch."""
+    B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
+    at T=4096; and NSA G=16 at T=32768 with L2 and MALL flushed before every launch."""
     res = {}
     B, H, T, D = 4, 16, 2048, 64
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
     out = torch.empty_like(q)
     fl = tra_useful_flops(B, H, T, D)
     for pw in (1.0, 2.0, 1.5):
-        st = stats(time_launches(lambda: cat.tra_fwd(q, k, v, 1.0, pw, out=out), 10, 20))
+        st = timed(lambda: cat.tra_fwd(q, k, v, 1.0, pw, out=out), batch=200)
         tf = fl / (st["ms"] * 1e-3) / 1e12
         res[f"tra_fwd B4 H16 T2048 D64 p{pw:g}"] = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(1, 2, 256, 64, dtype=torch.float32, seed=0))
     out = torch.empty_like(q)
-    res["tra_fwd_f32 B1 H2 T256 D64 p2"] = stats(
-        time_launches(lambda: cat.tra_fwd_f32(q, k, v, 1.0, 2.0, out=out), 10, 20))
+    res["tra_fwd_f32 B1 H2 T256 D64 p2"] = timed(
+        lambda: cat.tra_fwd_f32(q, k, v, 1.0, 2.0, out=out), batch=200)
     c = inputs.CONFIGS["tda_bf16_T8192_D128"]
     B, H, T, D = c["B"], c["H"], c["T"], c["D"]
     t5 = [x.to(dev) for x in inputs.tda_inputs(B, H, T, D, seed=0)]
@@ -194,13 +217,23 @@ def extra_configs(dev, nsa_c5=None):
                      device=dev)
     out = torch.empty_like(t5[0])
     fl = 6.0 * D * B * H * T * (T + 1) / 2.0      # two score products and one weighted sum per pair
-    st = stats(time_launches(lambda: cat.tda_fwd(*t5, c["beta"], c["lam"], 2.0,
-                                                 normalize=c["normalize"], out=out, workspace=ws),
-                             10, 20))
+    st = timed(lambda: cat.tda_fwd(*t5, c["beta"], c["lam"], 2.0, normalize=c["normalize"],
+                                   out=out, workspace=ws), batch=20)
     tf = fl / (st["ms"] * 1e-3) / 1e12
     res["tda_fwd B2 H32 T8192 D128 normalised beta=D^-1/2 lambda=0.5 p2 (6D FLOP per pair)"] = dict(
         st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
     del t5, ws, out
+    # TRA backward at the forward's measured shape
+    B, H, T, D = 2, 32, 8192, 128
+    q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
+    do = torch.randn(B, H, T, D, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev)
+    g = [torch.empty_like(q) for _ in range(3)]
+    fl = 10.0 * D * B * H * T * (T + 1) / 2.0     # five products per pair (S, dP, dV, dK, dQ)
+    st = timed(lambda: cat.tra_bwd(q, k, v, do, 1.0, 2.0, dq=g[0], dk=g[1], dv=g[2]), 5, 10, 10)
+    tf = fl / (st["ms"] * 1e-3) / 1e12
+    res["tra_bwd B2 H32 T8192 D128 beta1 p2 (10D FLOP per pair)"] = dict(
+        st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
+    del q, k, v, do, g
     B, Hq, Hkv, T, D, bs, S = 2, 32, 4, 4096, 128, 64, 16
     qn, kn, vn = (x.to(dev) for x in inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0))
     idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
@@ -208,7 +241,7 @@ def extra_configs(dev, nsa_c5=None):
     o = torch.empty_like(qn)
     lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
     gb = nsa_gathered_bytes(idx, T, bs, D)
-    st = stats(time_launches(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), 10, 20))
+    st = timed(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), batch=50)
     res["nsa_sel_fwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"] = dict(
         st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
     if nsa_c5 is not None:

@@ -43,6 +43,8 @@ def load_library():
     lib.tra_fwd.restype = ci
     lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_fwd_f32.restype = ci
+    lib.tra_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
+    lib.tra_bwd.restype = ci
     lib.tda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                             ci, ci, ci, ci, cf, cf, cf, ci, vp]
     lib.tda_fwd.restype = ci
@@ -107,6 +109,32 @@ def tra_fwd(q, k, v, beta, p, out=None, stream=None):
 def tra_fwd_f32(q, k, v, beta, p, out=None, stream=None):
     """Threshold Rectified Attention forward, fp32 in / fp32 out."""
     return _tra("tra_fwd_f32", torch.float32, q, k, v, beta, p, out, stream)
+
+
+def tra_bwd(q, k, v, dout, beta, p, dq=None, dk=None, dv=None, stream=None):
+    """Threshold Rectified Attention backward, bf16 in / bf16 out.
+
+    q, k, v, dout: contiguous bfloat16 [B, H, T, D] on the GPU.  Returns (dq, dk, dv).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(t, n, torch.bfloat16)
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, dout)):
+        raise ValueError("q, k, v, dout must all be [B, H, T, D]")
+    grads = []
+    for g, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if g is None:
+            g = torch.empty_like(q)
+        _check(g, n, torch.bfloat16)
+        if g.shape != q.shape:
+            raise ValueError(f"{n} must match q's shape")
+        grads.append(g)
+    B, H, T, D = q.shape
+    rc = load_library().tra_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                *(g.data_ptr() for g in grads), B, H, T, D, float(beta),
+                                float(p), _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("tra_bwd", rc)
+    return tuple(grads)
 
 
 def tda_workspace_bytes(B, H, T, D, normalize=True) -> int:

@@ -34,7 +34,8 @@ CXXFLAGS = [
 # vector registers the epilogue reads (the allocator then keeps the loop-invariant
 # Q operands in the accumulation registers instead).
 _THRESHOLD_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
-EXTRA = {"tra_fwd.hip": _THRESHOLD_FLAGS, "tda_fwd.hip": _THRESHOLD_FLAGS}
+EXTRA = {"tra_fwd.hip": _THRESHOLD_FLAGS, "tda_fwd.hip": _THRESHOLD_FLAGS,
+         "tra_bwd.hip": _THRESHOLD_FLAGS}
 
 
 def _hipcc() -> str:

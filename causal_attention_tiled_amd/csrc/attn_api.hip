@@ -58,6 +58,22 @@ ATTN_EXPORT int tra_fwd_f32(const float *q, const float *k, const float *v, floa
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+ATTN_EXPORT int tra_bwd(const void *q, const void *k, const void *v, const void *dout, void *dq,
+                        void *dk, void *dv, int B, int H, int T, int D, float beta, float p,
+                        void *stream) {
+    bool noop;
+    const int st = tra_validate(q, k, v, dq, B, H, T, D, beta, p, attn::kTraBwdDkvRows, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if (!dout || !dk || !dv) return ATTN_ERR_NULL;
+    if (misaligned(dout) || misaligned(dk) || misaligned(dv)) return ATTN_ERR_ALIGN;
+    const hipError_t e = attn::launch_tra_bwd_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), static_cast<const uint16_t *>(dout),
+        static_cast<uint16_t *>(dq), static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv),
+        B * H, T, D, beta, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 ATTN_EXPORT size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize) {
     if (!normalize || B <= 0 || H <= 0 || T <= 0 || D <= 0) return 0;
     return (size_t)2 * (size_t)B * (size_t)H * (size_t)T * (size_t)D * 2;

@@ -49,6 +49,10 @@ constexpr int kTraBf16Rows = 256;
 constexpr int kTraF32Rows = 64;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;
+// Query rows (dq kernel) and key rows (dk/dv kernel) per workgroup of the
+// Threshold Rectified Attention backward.
+constexpr int kTraBwdDqRows = 128;
+constexpr int kTraBwdDkvRows = 128;
 
 // Host-side launchers (one per kernel family); they pick the template
 // instance and return the HIP launch status.
@@ -57,6 +61,9 @@ hipError_t launch_tra_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                hipStream_t stream);
 hipError_t launch_tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
                               int BH, int T, int D, float beta, float p, hipStream_t stream);
+hipError_t launch_tra_bwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                               int BH, int T, int D, float beta, float p, hipStream_t stream);
 hipError_t launch_tda_fwd_bf16(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,
                                const uint16_t *k2, const uint16_t *v, uint16_t *out,
                                uint16_t *workspace, int BH, int T, int D, float beta,

@@ -1,0 +1,492 @@
+// tra_bwd.hip -- Threshold Rectified Attention backward for gfx950.
+//
+// Definition (snap-research/TDA, page "triton_threshold_attention.py",
+// `_threshold_rela_bwd_kernel_dq`, `_threshold_rela_bwd_kernel_dkv` and
+// `ThresholdRelaFunction.backward`): with x_ij = q_i.k_j - tau_i over the causal
+// pairs j <= i, w_ij = max(x_ij, 0)^p and g_ij = p * max(x_ij, 0)^(p-1) (0 for
+// x_ij <= 0), and a_ij = (dout_i . v_j) * g_ij,
+//     dq_i = sum_{j<=i} a_ij k_j,   dk_j = sum_{i>=j} a_ij q_i,   dv_j = sum_{i>=j} w_ij dout_i.
+// Gradients of q, k and v only (beta and p get none), in the input dtype.
+//
+// Two kernels, as on the page, so that every gradient row is written by exactly
+// one wavefront (no atomics; the result does not depend on scheduling):
+//  * tra_bwd_dq_kernel: the forward's layout with 128 query rows per workgroup (4
+//    wavefronts of 32 rows, one per SIMD: the Q and dO operands, the dQ
+//    accumulator and three operand streams need more than half of a SIMD's
+//    registers), transposed score tiles so tau and the mask are per lane.  Per 32-key block: S^T = K Q^T, dP^T = V dO^T, then
+//    A^T = dP^T * g (rounded to bf16, in the accumulator's register order) and
+//    dQ^T += K^T A^T with K^T read transposed from LDS.  K and V tiles stream
+//    HBM -> LDS by DMA, double-buffered, as in the forward.
+//  * tra_bwd_dkv_kernel: 128 key rows per workgroup, 4 wavefronts of 32 keys, one
+//    per SIMD (the dK and dV accumulators take 128 registers per lane).  A wave
+//    keeps its K and V rows in registers; Q and dO tiles of 64 queries stream
+//    through LDS.  Per 32-query block: S = -tau + Q K^T and dP = dO V^T (one key
+//    per lane, so the query thresholds come from a small LDS table), W and A
+//    rounded to bf16, then dV^T += dO^T W and dK^T += Q^T A with dO^T and Q^T read
+//    transposed from LDS.
+// The constant factor p of g is applied once to dq and dk at the end.
+#include <type_traits>
+
+#include "attn_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr int kDqWaves = 4;   // dq kernel: 32 query rows per wave, one wave per SIMD
+static_assert(kDqWaves * 32 == kTraBwdDqRows, "dq workgroup rows");
+constexpr int kDkvWaves = 4;  // dk/dv kernel: 32 key rows per wave
+static_assert(kDkvWaves * 32 == kTraBwdDkvRows, "dk/dv workgroup rows");
+constexpr int kBN = 64;       // keys (dq kernel) or queries (dk/dv kernel) per LDS tile
+
+// max(x, 0)^(p-1) for x > 0, else 0 (the factor p is applied to the sums).
+template <int PM>
+__device__ __forceinline__ float relu_pow_m1(float x, float p) {
+    if constexpr (PM == kPowOne) {
+        return x > 0.0f ? 1.0f : 0.0f;
+    } else if constexpr (PM == kPowTwo) {
+        return fmaxf(x, 0.0f);
+    } else {
+        return x > 0.0f ? __builtin_amdgcn_exp2f((p - 1.0f) * __builtin_amdgcn_logf(x)) : 0.0f;
+    }
+}
+
+// Workgroup id -> (head slab, key tile) for the dk/dv kernel: key tiles with the
+// most queries after them (small index) first; heads split over the 8 XCDs as in
+// tile_order.
+__device__ __forceinline__ void key_tile_order(int bid, int BH, int nkt, int &bh, int &kt) {
+    if ((BH & 7) == 0) {
+        const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
+        bh = xcd * hpx + s % hpx;
+        kt = s / hpx;
+    } else {
+        bh = bid % BH;
+        kt = bid / BH;
+    }
+}
+
+template <int D, int PM>
+__global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ,
+    int BH, int T, int nqt, float beta, float p) {
+    constexpr int BM = kDqWaves * 32;
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;
+    constexpr int TILEB = kBN * ROWB;
+    constexpr int BLKB = 32 * ROWB;
+    constexpr int LOADS = kBN * CH / (64 * kDqWaves);
+    constexpr int NDS = D / 16;
+    constexpr int NDT = D / 32;
+    constexpr int KB = 0, VB = 2 * TILEB;  // K tiles (2 buffers), then V tiles
+    static_assert(LOADS >= 1 && kBN * CH % (64 * kDqWaves) == 0, "tile staging");
+    static_assert(TILEB == kDqWaves * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TILEB];
+
+    int bh, qt;
+    tile_order(blockIdx.x, BH, nqt, bh, qt);
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    qt = __builtin_amdgcn_readfirstlane(qt);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const size_t slab = (size_t)bh * T * D;
+    const int q0 = qt * BM;
+    const int qw0 = q0 + 32 * wave;
+    const int q_last = min(q0 + BM, T) - 1;
+    const int ntiles = q_last / kBN + 1;
+
+    const u32x4 rk = make_rsrc(K + slab, (uint32_t)T * ROWB);
+    const u32x4 rv = make_rsrc(V + slab, (uint32_t)T * ROWB);
+    int dma_src[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int pos = (wave * LOADS + j) * 1024 + lane * 16;
+        const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
+        dma_src[j] = row * ROWB + ((slot ^ tile_swz<D>(row)) << 4);
+    }
+    auto gload = [&](int n, int buf) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int dst = buf * TILEB + (wave * LOADS + j) * 1024;
+            dma16(rk, &lds[KB + dst], dma_src[j], n * TILEB);
+            dma16(rv, &lds[VB + dst], dma_src[j], n * TILEB);
+        }
+    };
+
+    // row-operand reads (K or V rows l32, chunk 2*ds + hi) and transposed K reads
+    int koff[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) koff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz<D>(l32)) << 4);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int trow = 4 * (g16 >> 1) + (s16 >> 2);
+    int toff[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 8 * h;
+            toff[dt][h] = row * ROWB +
+                          (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
+                          8 * (s16 & 1);
+        }
+    auto row_frag = [&](int base, int buf, int kb, int ds) {
+        return *(const bf16x8 *)(&lds[koff[ds] + base + buf * TILEB + kb * BLKB]);
+    };
+    // K^T operand for keys 16c + {4hi..4hi+3, 8+4hi..8+4hi+3} of the block, dims 32dt + lane%32
+    auto kt_frag = [&](int buf, int kb, int dt, int c) {
+        const uint8_t *base = &lds[KB + buf * TILEB + kb * BLKB + 16 * c * ROWB];
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + toff[dt][0]));
+        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(base + toff[dt][1]));
+        return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x16 dqacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqacc[dt][r] = 0.0f;
+
+    gload(0, 0);
+    const int myq = qw0 + l32;
+    bf16x8 qf[NDS], df[NDS];
+    {
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 a = zero4, b = zero4;
+            if (myq < T) {
+                a = *(const u32x4 *)(Q + slab + (size_t)myq * D + ds * 16 + hi * 8);
+                b = *(const u32x4 *)(dO + slab + (size_t)myq * D + ds * 16 + hi * 8);
+            }
+            qf[ds] = as_bf16x8(a);
+            df[ds] = as_bf16x8(b);
+        }
+    }
+    const float tau = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
+    f32x16 zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+
+    auto mask_block = [&](f32x16 &sv, int kbase) {
+        const int lim = qw0 + l32 - kbase - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) > lim) sv[r] = -INFINITY;
+    };
+    auto tile_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // Per 32-key block, four phases:
+    //   1: S^T = K Q^T                          (V operand read alongside)
+    //   2: dP^T = V dO^T || S^T <- max(S^T - tau, 0)^(p-1)
+    //   3: A^T = bf16(dP^T * S^T)                (K^T operand read alongside)
+    //   4: dQ^T += K^T A^T                       (next block's K operand read alongside)
+    auto tile = [&](int n, auto masked, int buf) {
+        constexpr bool kMasked = decltype(masked)::value;
+        if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
+        if constexpr (kMasked) {
+            if (n * kBN > qw0 + 31) {
+                tile_sync();
+                return;
+            }
+        }
+        bf16x8 kf[NDS], vf[NDS], ktf[NDT][2], af[2];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kf[ds] = row_frag(KB, buf, 0, ds);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = zero16, dp = zero16;
+            // 1
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) vf[ds] = row_frag(VB, buf, kb, ds);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(kf[ds], qf[ds], s);
+#pragma unroll
+            for (int i = 0; i < NDS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kMasked) mask_block(s, n * kBN + 32 * kb);
+            // 2
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(vf[ds], df[ds], dp);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = relu_pow_m1<PM>(s[r] - tau, p);
+#pragma unroll
+            for (int i = 0; i < NDS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // 3
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) ktf[dt][c] = kt_frag(buf, kb, dt, c);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) af[r >> 3][r & 7] = (__bf16)(dp[r] * s[r]);
+            __builtin_amdgcn_sched_barrier(0);
+            // 4
+            if (kb == 0) {
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) kf[ds] = row_frag(KB, buf, 1, ds);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = mfma_32x32x16(ktf[dt][c], af[c], dqacc[dt]);
+            if (kb == 0) {
+#pragma unroll
+                for (int i = 0; i < 2 * NDT; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        tile_sync();
+    };
+
+    const int n_interior = min(ntiles, (qw0 + 1) / kBN);
+    const std::false_type plain{};
+    const std::true_type masked{};
+    int n = 0;
+    for (; n + 1 < n_interior; n += 2) {
+        tile(n, plain, 0);
+        tile(n + 1, plain, 1);
+    }
+    if (n < n_interior) tile(n++, plain, 0);
+    if (n < ntiles && (n & 1)) tile(n++, masked, 1);
+    for (; n + 1 < ntiles; n += 2) {
+        tile(n, masked, 0);
+        tile(n + 1, masked, 1);
+    }
+    if (n < ntiles) tile(n++, masked, 0);
+
+    // dQ^T accumulator: lane holds row qw0 + l32, dims 32*dt + 8*i + 4*hi + j.
+    if (myq < T) {
+        uint16_t *row = dQ + slab + (size_t)myq * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 pr = {pack_bf16x2(p * dqacc[dt][4 * i], p * dqacc[dt][4 * i + 1]),
+                                  pack_bf16x2(p * dqacc[dt][4 * i + 2], p * dqacc[dt][4 * i + 3])};
+                *(u32x2 *)(row + dt * 32 + 8 * i + 4 * hi) = pr;
+            }
+    }
+}
+
+template <int D, int PM>
+__global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int BH, int T, int nkt, float beta, float p) {
+    constexpr int BK = kDkvWaves * 32;               // key rows per workgroup
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;
+    constexpr int TILEB = kBN * ROWB;                // one tile of 64 query rows
+    constexpr int BLKB = 32 * ROWB;
+    constexpr int LOADS = kBN * CH / (64 * kDkvWaves);
+    constexpr int NDS = D / 16;
+    constexpr int NDT = D / 32;
+    constexpr int QB = 0, OB = 2 * TILEB;            // Q tiles (2 buffers), then dO tiles
+    static_assert(LOADS >= 1 && kBN * CH % (64 * kDkvWaves) == 0, "tile staging");
+    static_assert(TILEB == kDkvWaves * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TILEB];
+    __shared__ __attribute__((aligned(16))) float ntau[2][kBN];  // -tau of each query of a tile
+
+    int bh, kt;
+    key_tile_order(blockIdx.x, BH, nkt, bh, kt);
+    bh = __builtin_amdgcn_readfirstlane(bh);
+    kt = __builtin_amdgcn_readfirstlane(kt);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const size_t slab = (size_t)bh * T * D;
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * wave;                  // this wave's keys kw0 .. kw0+31
+    const int mykey = kw0 + l32;
+    const int n0 = k0 / kBN;                         // first query tile with a query >= k0
+    const int ntiles = (T - 1) / kBN + 1;
+    const int jd = kw0 / 32;                         // this wave's diagonal 32-query block
+
+    const u32x4 rq = make_rsrc(Q + slab, (uint32_t)T * ROWB);
+    const u32x4 ro = make_rsrc(dO + slab, (uint32_t)T * ROWB);
+    int dma_src[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int pos = (wave * LOADS + j) * 1024 + lane * 16;
+        const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
+        dma_src[j] = row * ROWB + ((slot ^ tile_swz<D>(row)) << 4);
+    }
+    const float tscale = 2.0f / (float)D;
+    auto gload = [&](int n, int buf) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int dst = buf * TILEB + (wave * LOADS + j) * 1024;
+            dma16(rq, &lds[QB + dst], dma_src[j], n * TILEB);
+            dma16(ro, &lds[OB + dst], dma_src[j], n * TILEB);
+        }
+        if (wave == 0) ntau[buf][lane] = -beta * sqrtf(tscale * logf((float)(n * kBN + lane + 1)));
+    };
+
+    int roff[NDS];  // Q or dO rows l32, chunk 2*ds + hi
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz<D>(l32)) << 4);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int trow = 4 * (g16 >> 1) + (s16 >> 2);
+    int toff[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 8 * h;
+            toff[dt][h] = row * ROWB +
+                          (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
+                          8 * (s16 & 1);
+        }
+    auto row_frag = [&](int base, int buf, int qb, int ds) {
+        return *(const bf16x8 *)(&lds[roff[ds] + base + buf * TILEB + qb * BLKB]);
+    };
+    // transposed operand (dO^T or Q^T) for queries 16c + {4hi..4hi+3, 8+4hi..8+4hi+3}
+    // of the block, dims 32dt + lane%32
+    auto t_frag = [&](int base, int buf, int qb, int dt, int c) {
+        const uint8_t *b = &lds[base + buf * TILEB + qb * BLKB + 16 * c * ROWB];
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(b + toff[dt][0]));
+        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(b + toff[dt][1]));
+        return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x16 dkacc[NDT], dvacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[dt][r] = dvacc[dt][r] = 0.0f;
+
+    gload(n0, 0);
+    // this wave's key and value rows as the B operands (lane = key, 8 dims per k-step)
+    bf16x8 kf[NDS], vf[NDS];
+    {
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 a = zero4, b = zero4;
+            if (mykey < T) {
+                a = *(const u32x4 *)(K + slab + (size_t)mykey * D + ds * 16 + hi * 8);
+                b = *(const u32x4 *)(V + slab + (size_t)mykey * D + ds * 16 + hi * 8);
+            }
+            kf[ds] = as_bf16x8(a);
+            vf[ds] = as_bf16x8(b);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+
+    f32x16 zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
+    // diagonal block: key kw0 + l32 against query kw0 + 8*(r/4) + 4*hi + r%4
+    auto mask_diag = [&](f32x16 &sv) {
+        const int lim = l32 - 4 * hi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (lim > 8 * (r >> 2) + (r & 3)) sv[r] = -INFINITY;
+    };
+
+    for (int n = n0; n < ntiles; ++n) {
+        const int buf = (n - n0) & 1;
+        if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int jb = 2 * n + qb;  // global 32-query block
+            if (jb < jd) continue;      // every query of the block precedes every key of the wave
+            // S = -tau + Q K^T, with -tau of the register's query as the initial value
+            f32x16 s;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 t4 = *(const f32x4 *)(&ntau[buf][32 * qb + 8 * g + 4 * hi]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[4 * g + j] = t4[j];
+            }
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(row_frag(QB, buf, qb, ds), kf[ds], s);
+            f32x16 dp = zero16;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(row_frag(OB, buf, qb, ds), vf[ds], dp);
+            if (jb == jd) mask_diag(s);
+            bf16x8 wf[2], af[2];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                wf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(s[r], p);
+                af[r >> 3][r & 7] = (__bf16)(dp[r] * relu_pow_m1<PM>(s[r], p));
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    dvacc[dt] = mfma_32x32x16(t_frag(OB, buf, qb, dt, c), wf[c], dvacc[dt]);
+                    dkacc[dt] = mfma_32x32x16(t_frag(QB, buf, qb, dt, c), af[c], dkacc[dt]);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+    }
+
+    // dK^T, dV^T accumulators: lane holds key kw0 + l32, dims 32*dt + 8*i + 4*hi + j.
+    if (mykey < T) {
+        uint16_t *krow = dK + slab + (size_t)mykey * D;
+        uint16_t *vrow = dV + slab + (size_t)mykey * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 kp = {pack_bf16x2(p * dkacc[dt][4 * i], p * dkacc[dt][4 * i + 1]),
+                                  pack_bf16x2(p * dkacc[dt][4 * i + 2], p * dkacc[dt][4 * i + 3])};
+                const u32x2 vp = {pack_bf16x2(dvacc[dt][4 * i], dvacc[dt][4 * i + 1]),
+                                  pack_bf16x2(dvacc[dt][4 * i + 2], dvacc[dt][4 * i + 3])};
+                *(u32x2 *)(krow + dt * 32 + 8 * i + 4 * hi) = kp;
+                *(u32x2 *)(vrow + dt * 32 + 8 * i + 4 * hi) = vp;
+            }
+    }
+}
+
+template <int D, int PM>
+hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                  uint16_t *dq, uint16_t *dk, uint16_t *dv, int BH, int T, float beta, float p,
+                  hipStream_t stream) {
+    int nqt = (T + kTraBwdDqRows - 1) / kTraBwdDqRows;
+    void *a1[] = {&q, &k, &v, &dout, &dq, &BH, &T, &nqt, &beta, &p};
+    hipError_t e = hipLaunchKernel((const void *)tra_bwd_dq_kernel<D, PM>,
+                                   dim3((unsigned)(BH * nqt)), dim3(64 * kDqWaves), a1, 0, stream);
+    if (e != hipSuccess) return e;
+    int nkt = (T + kTraBwdDkvRows - 1) / kTraBwdDkvRows;
+    void *a2[] = {&q, &k, &v, &dout, &dk, &dv, &BH, &T, &nkt, &beta, &p};
+    return hipLaunchKernel((const void *)tra_bwd_dkv_kernel<D, PM>, dim3((unsigned)(BH * nkt)),
+                           dim3(64 * kDkvWaves), a2, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_tra_bwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                               int BH, int T, int D, float beta, float p, hipStream_t stream) {
+    const int pm = p == 1.0f ? kPowOne : (p == 2.0f ? kPowTwo : kPowGeneral);
+    if (D == 128) {
+        if (pm == kPowTwo) return launch<128, kPowTwo>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+        if (pm == kPowOne) return launch<128, kPowOne>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+        return launch<128, kPowGeneral>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+    }
+    if (pm == kPowTwo) return launch<64, kPowTwo>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+    if (pm == kPowOne) return launch<64, kPowOne>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+    return launch<64, kPowGeneral>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+}
+
+}  // namespace attn

@@ -78,6 +78,33 @@ int tra_fwd_f32(const float *q, const float *k, const float *v, float *out,
                 int B, int H, int T, int D, float beta, float p, void *stream);
 
 /*
+ * Threshold Rectified Attention backward, bf16 in / bf16 out.
+ *
+ * Source: snap-research/TDA, page "triton_threshold_attention.py" --
+ * `_threshold_rela_bwd_kernel_dq`, `_threshold_rela_bwd_kernel_dkv` and
+ * `ThresholdRelaFunction.backward` (gradients of q, k and v of the forward
+ * above; none for beta or p; returned in the input dtype).
+ *
+ * With x_ij = q_i . k_j - tau_i over the causal pairs j <= i (masked pairs
+ * contribute nothing), w_ij = max(x_ij, 0)^p, g_ij = p * x_ij^(p-1) for
+ * x_ij > 0 (else 0) and a_ij = (dout_i . v_j) * g_ij:
+ *   dq_i = sum_{j<=i} a_ij k_j,  dk_j = sum_{i>=j} a_ij q_i,  dv_j = sum_{i>=j} w_ij dout_i
+ *
+ *   q, k, v, dout : bf16 [B, H, T, D]      (read only)
+ *   dq, dk, dv    : bf16 [B, H, T, D]      (written; may not alias the inputs or
+ *                                            each other)
+ *   D, beta, p    : as tra_fwd
+ *
+ * Numerics: scores and dout.v in fp32 from bf16 products; w and a rounded to
+ * bf16 before the products that consume them; fp32 accumulation; gradients
+ * rounded to bf16.  Every gradient row is written by one wavefront (no
+ * atomics): results are deterministic.
+ */
+int tra_bwd(const void *q, const void *k, const void *v, const void *dout,
+            void *dq, void *dk, void *dv,
+            int B, int H, int T, int D, float beta, float p, void *stream);
+
+/*
  * Threshold Differential Attention forward, bf16 in / bf16 out.
  *
  * Source: snap-research/TDA, page "triton_threshold_attention.py" --

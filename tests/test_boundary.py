@@ -31,8 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("tra_fwd", "tra_fwd_f32", "tda_fwd", "tda_workspace_bytes", "nsa_sel_fwd",
-              "attn_status_str"):
+    for n in ("tra_fwd", "tra_fwd_f32", "tra_bwd", "tda_fwd", "tda_workspace_bytes",
+              "nsa_sel_fwd", "attn_status_str"):
         assert n in names
 
 
@@ -94,6 +94,22 @@ def test_nsa_validation(lib):
     assert _nsa(lib, lse=P + 1) == EALIGN
     assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, T=0) == OK
     assert _nsa(lib, q=None, k=None, v=None, idx=None, o=None, lse=None, B=0) == OK
+
+
+def _bwd(lib, q=P, k=P, v=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, T=8, D=128, beta=1.0, p=2.0):
+    return lib.tra_bwd(q, k, v, do, dq, dk, dv, B, H, T, D, beta, p, None)
+
+
+def test_tra_bwd_validation(lib):
+    assert _bwd(lib, do=None) == ENULL
+    assert _bwd(lib, dq=None) == ENULL
+    assert _bwd(lib, dv=None) == ENULL
+    assert _bwd(lib, T=-1) == ESHAPE
+    assert _bwd(lib, p=0.0) == ESHAPE
+    assert _bwd(lib, beta=float("nan")) == ESHAPE
+    assert _bwd(lib, D=32) == EUNSUP
+    assert _bwd(lib, dk=P + 2) == EALIGN
+    assert _bwd(lib, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, B=0) == OK
 
 
 def _tda(lib, q1=P, q2=P, k1=P, k2=P, v=P, o=P, ws=P, ws_bytes=1 << 40, B=1, H=1, T=8, D=128,

@@ -1,0 +1,123 @@
+"""GPU parity of the Threshold Rectified Attention backward (tra_bwd) against the
+fp64 oracle on the same seeded inputs, plus GPU-only properties that must hold bit
+for bit (determinism, causal dependency structure)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import causal_attention_tiled_amd as cat
+from causal_attention_tiled_amd import inputs
+
+from _parity import BF16_REL, assert_rows_close, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _dout(B, H, T, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, H, T, D, generator=g).to(torch.bfloat16)
+
+
+def _run(q, k, v, do, beta, p, dev):
+    g = cat.tra_bwd(q.to(dev), k.to(dev), v.to(dev), do.to(dev), beta, p)
+    torch.cuda.synchronize()
+    return [x.cpu() for x in g]
+
+
+SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 1, 129, 64), (1, 2, 300, 128),
+         (2, 1, 520, 64), (1, 1, 777, 128)]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+def test_tra_bwd_small(gpu, shape, p):
+    B, H, T, D = shape
+    print(f"tra_bwd {shape} p={p}", flush=True)
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=T + D)
+    do = _dout(B, H, T, D, seed=T)
+    got = _run(q, k, v, do, 1.0, p, gpu)
+    ref = oracle.tra_bwd_ref(q, k, v, do, 1.0, p)
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        assert_rows_close(g, r, BF16_REL, f"{n} {shape} p={p}")
+
+
+@pytest.mark.parametrize("beta,p", [(0.0, 2.0), (-0.5, 2.0), (2.0, 2.0), (0.0, 3.0), (-0.5, 3.0),
+                                    (2.0, 3.0), (-0.5, 1.5)])
+def test_tra_bwd_beta_p(gpu, beta, p):
+    B, H, T, D = 1, 2, 200, 128
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=31)
+    do = _dout(B, H, T, D, seed=32)
+    got = _run(q, k, v, do, beta, p, gpu)
+    ref = oracle.tra_bwd_ref(q, k, v, do, beta, p)
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        assert_rows_close(g, r, BF16_REL, f"{n} beta={beta} p={p}")
+
+
+def test_tra_bwd_p_below_one_well_conditioned(gpu):
+    """p = 0.5: the weight's derivative p*x^(p-1) is unbounded as x -> 0+, so near the
+    threshold a gradient follows the last bits of the fp32 score and no fixed tolerance
+    holds.  With beta = -40 every pair of rows i >= 1 sits at x = q.k + 40*sqrt(2 ln(i+1)/D)
+    >= 4 above it (the scores are about N(0, 1)), the well-conditioned case; row 0
+    (tau_0 = 0) and key 0, which row 0 feeds, are left out."""
+    B, H, T, D = 1, 2, 200, 128
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=33)
+    do = _dout(B, H, T, D, seed=34)
+    got = _run(q, k, v, do, -40.0, 0.5, gpu)
+    ref = oracle.tra_bwd_ref(q, k, v, do, -40.0, 0.5)
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        assert_rows_close(g[:, :, 1:], r[:, :, 1:], BF16_REL, f"{n} p=0.5")
+
+
+def test_tra_bwd_T8192_D128_sampled(gpu):
+    """B=2 H=32 T=8192 D=128, beta=1, p=2 (the forward's measured shape): all three
+    gradients on the GPU, sampled query rows (dq) and key rows (dk, dv) from the oracle."""
+    B, H, T, D = 2, 32, 8192, 128
+    print("tra_bwd T8192: inputs", flush=True)
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=0)
+    do = _dout(B, H, T, D, seed=1)
+    dq, dk, dv = _run(q, k, v, do, 1.0, 2.0, gpu)
+    for g in (dq, dk, dv):
+        assert torch.isfinite(g.float()).all()
+    qrows = sample_rows(B, H, T, 160, seed=3, extra_positions=(0, 31, 32, 127, 128, T - 1))
+    krows = sample_rows(B, H, T, 160, seed=4, extra_positions=(0, 31, 32, 127, 128, T - 1))
+    rq, rk, rv = oracle.tra_bwd_ref(q, k, v, do, 1.0, 2.0, qrows=qrows, krows=krows)
+    assert_rows_close(dq.reshape(-1, D)[qrows], rq, BF16_REL, "dq T8192 sampled")
+    assert_rows_close(dk.reshape(-1, D)[krows], rk, BF16_REL, "dk T8192 sampled")
+    assert_rows_close(dv.reshape(-1, D)[krows], rv, BF16_REL, "dv T8192 sampled")
+
+
+def test_tra_bwd_deterministic(gpu):
+    q, k, v = inputs.tra_inputs(2, 2, 700, 128, seed=5)
+    do = _dout(2, 2, 700, 128, seed=6)
+    a = _run(q, k, v, do, 1.0, 1.5, gpu)
+    b = _run(q, k, v, do, 1.0, 1.5, gpu)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_tra_bwd_causal_structure_bitexact(gpu):
+    """dq rows <= c ignore keys/values after c; dk, dv rows >= c ignore queries and
+    output gradients before c."""
+    B, H, T, D = 1, 2, 600, 128
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=7)
+    do = _dout(B, H, T, D, seed=8)
+    a = _run(q, k, v, do, 1.0, 2.0, gpu)
+    c = 300
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, c + 1:] = torch.randn_like(k2[:, :, c + 1:].float()).to(torch.bfloat16)
+    v2[:, :, c + 1:] = torch.randn_like(v2[:, :, c + 1:].float()).to(torch.bfloat16)
+    b = _run(q, k2, v2, do, 1.0, 2.0, gpu)
+    assert torch.equal(a[0][:, :, :c + 1], b[0][:, :, :c + 1])
+    q2, do2 = q.clone(), do.clone()
+    q2[:, :, :c] = torch.randn_like(q2[:, :, :c].float()).to(torch.bfloat16)
+    do2[:, :, :c] = torch.randn_like(do2[:, :, :c].float()).to(torch.bfloat16)
+    b = _run(q2, k, v, do2, 1.0, 2.0, gpu)
+    assert torch.equal(a[1][:, :, c:], b[1][:, :, c:])
+    assert torch.equal(a[2][:, :, c:], b[2][:, :, c:])
+
+
+def test_tra_bwd_empty_is_noop(gpu):
+    z = torch.empty(1, 2, 0, 64, dtype=torch.bfloat16, device=gpu)
+    dq, dk, dv = cat.tra_bwd(z, z, z, z, 1.0, 2.0)
+    assert dq.shape == z.shape
