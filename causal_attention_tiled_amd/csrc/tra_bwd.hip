@@ -401,40 +401,102 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
             if (lim > 8 * (r >> 2) + (r & 3)) sv[r] = -INFINITY;
     };
 
+    // Per 32-query block, four phases, each with the operands of the next one read
+    // alongside its MFMAs:
+    //   1: S = -tau + Q K^T            (dO rows read)
+    //   2: dP = dO V^T || W, G from S  (dO^T read)
+    //   3: dV^T += dO^T W || A = dP G  (Q^T read)
+    //   4: dK^T += Q^T A               (the next block's Q rows and -tau read)
+    bf16x8 qrow[NDS], orow[NDS], tf[NDT][2];
+    f32x16 sinit;
+    auto read_q = [&](int buf, int qb) {
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) qrow[ds] = row_frag(QB, buf, qb, ds);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 t4 = *(const f32x4 *)(&ntau[buf][32 * qb + 8 * g + 4 * hi]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sinit[4 * g + j] = t4[j];
+        }
+    };
     for (int n = n0; n < ntiles; ++n) {
         const int buf = (n - n0) & 1;
         if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
+        bool have_q = false;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int jb = 2 * n + qb;  // global 32-query block
             if (jb < jd) continue;      // every query of the block precedes every key of the wave
-            // S = -tau + Q K^T, with -tau of the register's query as the initial value
-            f32x16 s;
+            if (!have_q) read_q(buf, qb);
+            // 1
+            f32x16 s = sinit;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 t4 = *(const f32x4 *)(&ntau[buf][32 * qb + 8 * g + 4 * hi]);
+            for (int ds = 0; ds < NDS; ++ds) orow[ds] = row_frag(OB, buf, qb, ds);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s[4 * g + j] = t4[j];
+            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(qrow[ds], kf[ds], s);
+#pragma unroll
+            for (int i = 0; i < NDS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(row_frag(QB, buf, qb, ds), kf[ds], s);
-            f32x16 dp = zero16;
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(row_frag(OB, buf, qb, ds), vf[ds], dp);
+            __builtin_amdgcn_sched_barrier(0);
             if (jb == jd) mask_diag(s);
-            bf16x8 wf[2], af[2];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                wf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(s[r], p);
-                af[r >> 3][r & 7] = (__bf16)(dp[r] * relu_pow_m1<PM>(s[r], p));
-            }
+            // 2
+            f32x16 dp = zero16;
+            bf16x8 wf[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    dvacc[dt] = mfma_32x32x16(t_frag(OB, buf, qb, dt, c), wf[c], dvacc[dt]);
-                    dkacc[dt] = mfma_32x32x16(t_frag(QB, buf, qb, dt, c), af[c], dkacc[dt]);
+                for (int dt = 0; dt < NDT; ++dt) tf[dt][c] = t_frag(OB, buf, qb, dt, c);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(orow[ds], vf[ds], dp);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                wf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(s[r], p);
+                s[r] = relu_pow_m1<PM>(s[r], p);
+            }
+#pragma unroll
+            for (int i = 0; i < NDS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // 3
+            bf16x8 af[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) dvacc[dt] = mfma_32x32x16(tf[dt][c], wf[c], dvacc[dt]);
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) tf[dt][c] = t_frag(QB, buf, qb, dt, c);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) af[r >> 3][r & 7] = (__bf16)(dp[r] * s[r]);
+#pragma unroll
+            for (int i = 0; i < 2 * NDT; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // 4
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) dkacc[dt] = mfma_32x32x16(tf[dt][c], af[c], dkacc[dt]);
+            have_q = false;
+            if (qb == 0) {
+                read_q(buf, 1);
+                have_q = true;
+#pragma unroll
+                for (int i = 0; i < 2 * NDT; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
