@@ -14,6 +14,10 @@ Functions
     Threshold Rectified Attention backward: (dq, dk, dv) in fp64 for the given
     query rows (dq) and key rows (dk, dv).  Source: the same page's backward
     kernels and autograd function (gradients of q, k, v).
+``nsa_bwd_ref(q, k, v, block_idx, block_size, dout, qrows=None, krows=None)``
+    NSA selection-branch backward: (dq, dk, dv) in fp64 for the given query rows
+    (dq, flat (b*Hq + h)*T + i) and key rows (dk, dv, flat (b*Hkv + kv)*T + j).
+    Built from the forward's definition (the page shows no backward).
 ``tda_ref(q1, q2, k1, k2, v, beta, lam, p, normalize=True, rows=None)``
     Threshold Differential Attention: optional L2 normalisation of the q and k
     rows, two Threshold Rectified Attention outputs over the same v, combined
@@ -80,6 +84,10 @@ def _load():
     lib.oracle_tra_bwd_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dbl,
                                         dbl, vp, i64, vp, vp, i64, vp, vp, ctypes.c_int]
     lib.oracle_tra_bwd_rows.restype = ctypes.c_int
+    lib.oracle_nsa_bwd_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i64, i64,
+                                        i64, i64, i64, vp, i64, vp, vp, i64, vp, vp,
+                                        ctypes.c_int]
+    lib.oracle_nsa_bwd_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -171,6 +179,48 @@ def tra_bwd_ref(q, k, v, dout, beta: float, p: float, qrows=None, krows=None,
     shape = (B, H, T, D)
     return (dq.reshape(shape) if qr is None else dq, dk.reshape(shape) if kr is None else dk,
             dv.reshape(shape) if kr is None else dv)
+
+
+def nsa_bwd_ref(q, k, v, block_idx, block_size: int, dout, qrows=None, krows=None,
+                nthreads: int = 0):
+    """NSA selection-branch backward in fp64.
+
+    q, dout: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: [B, Hkv, T, S] ints.
+    Returns (dq, dk, dv): full float64 tensors, or per-row arrays when qrows / krows
+    are given.
+    """
+    qa, dt = _as_input(q)
+    ka, dtk = _as_input(k)
+    va, dtv = _as_input(v)
+    oa, dto = _as_input(dout)
+    if not (dt == dtk == dtv == dto):
+        raise TypeError("q, k, v, dout must share one dtype")
+    if qa.ndim != 4 or ka.shape != va.shape or oa.shape != qa.shape:
+        raise ValueError("q, dout must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
+    B, Hq, T, D = qa.shape
+    Hkv = ka.shape[1]
+    idx = np.ascontiguousarray(np.asarray(block_idx, dtype=np.int32))
+    if idx.ndim != 4 or idx.shape[:3] != (B, Hkv, T):
+        raise ValueError("block_idx must be [B, Hkv, T, S]")
+    S = idx.shape[3]
+    qr, qp = _rows_arg(qrows)
+    kr, kp = _rows_arg(krows)
+    nq = B * Hq * T if qr is None else qr.size
+    nk = B * Hkv * T if kr is None else kr.size
+    dq = np.zeros((nq, D), dtype=np.float64)
+    dk = np.zeros((nk, D), dtype=np.float64)
+    dv = np.zeros((nk, D), dtype=np.float64)
+    rc = _load().oracle_nsa_bwd_rows(qa.ctypes.data, ka.ctypes.data, va.ctypes.data,
+                                     oa.ctypes.data, dt, idx.ctypes.data, B, Hq, Hkv, T, D,
+                                     int(block_size), S, qp, nq, dq.ctypes.data, kp, nk,
+                                     dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_nsa_bwd_rows rejected its arguments")
+    if qr is None:
+        dq = dq.reshape(B, Hq, T, D)
+    if kr is None:
+        dk, dv = dk.reshape(B, Hkv, T, D), dv.reshape(B, Hkv, T, D)
+    return dq, dk, dv
 
 
 def tda_ref(q1, q2, k1, k2, v, beta: float, lam: float, p: float, normalize: bool = True,

@@ -34,6 +34,12 @@
  *   (gradients of q, k and v only; with x = q_i.k_j - tau_i the weight's
  *   derivative is p * max(x, 0)^(p-1) for x > 0 and 0 otherwise).
  *
+ * NSA selection-branch backward
+ *   source: the same page's forward (its attended set, scale and softmax) and
+ *   its statement that the lse output feeds a backward pass that the page does
+ *   not show; the gradients here are those of that forward's definition with
+ *   respect to q, k and v (block_idx is an integer index, not differentiated).
+ *
  * Threshold Differential Attention
  *   source: snap-research/TDA, page "triton_threshold_attention.py",
  *   `differential_threshold_rela_triton` (optionally L2-normalise q1, k1, q2,
@@ -411,6 +417,172 @@ int oracle_tra_bwd_rows(const void *q, const void *k, const void *v, const void 
                 }
             }
         }
+    }
+    return bad ? -1 : 0;
+}
+
+/* The attended set of row (b, kv, i): chosen[blk] for each selected block id in
+ * range (duplicates once); returns the number of attended tokens (j <= i). */
+static int64_t nsa_attended(const int32_t *slots, int64_t S, int64_t nblk, int64_t bs,
+                            int64_t i, unsigned char *chosen) {
+    memset(chosen, 0, (size_t)(nblk > 0 ? nblk : 1));
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t blk = slots[s];
+        if (blk >= 0 && blk < nblk) chosen[blk] = 1;
+    }
+    int64_t na = 0;
+    for (int64_t blk = 0; blk < nblk; ++blk)
+        if (chosen[blk])
+            for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) ++na;
+    return na;
+}
+
+/* Softmax statistics of query row (b, h, i) over its attended set:
+ * M = max_j s_j and l = sum_j exp(s_j - M), s_j = scale * q_i . k_j; and
+ * delta = sum_j P_j (dout_i . v_j) with P_j = exp(s_j - M) / l.  Returns 0 if
+ * the set is empty (then nothing flows through the row). */
+static int nsa_row_stats(const void *q, const void *k, const void *v, const void *dout,
+                         int dtype, const unsigned char *chosen, int64_t nblk, int64_t bs,
+                         int64_t i, int64_t qrow, int64_t kvslab, int64_t D, double scale,
+                         double *M, double *l, double *delta) {
+    double m = -INFINITY;
+    int64_t na = 0;
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+        if (!chosen[blk]) continue;
+        for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
+            if (scale * dot > m) m = scale * dot;
+            ++na;
+        }
+    }
+    if (na == 0) return 0;
+    double sum = 0.0, dl = 0.0;
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+        if (!chosen[blk]) continue;
+        for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
+            double dot = 0.0, dp = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
+                dp += widen(dout, dtype, qrow + d) * widen(v, dtype, kvslab + j * D + d);
+            }
+            const double e = exp(scale * dot - m);
+            sum += e;
+            dl += e * dp;
+        }
+    }
+    *M = m;
+    *l = sum;
+    *delta = dl / sum;
+    return 1;
+}
+
+/*
+ * NSA selection-branch backward for a list of query rows (dq) and key rows (dk, dv).
+ *
+ *   q, dout    : [B, Hq, T, D];  k, v : [B, Hkv, T, D]  (dtype)
+ *   block_idx  : [B, Hkv, T, S] int32, as for the forward
+ *   qrows, nq  : flat rows (b*Hq + h)*T + i (NULL: all), dq [nq, D] (may be NULL)
+ *   krows, nk  : flat rows (b*Hkv + kv)*T + j (NULL: all), dk, dv [nk, D] (may be NULL)
+ *
+ * With A_i the attended set of row i (as in the forward), s_ij = scale q_i.k_j,
+ * P_ij = softmax over A_i, dP_ij = dout_i . v_j, delta_i = sum_{j in A_i} P_ij dP_ij
+ * and dS_ij = P_ij (dP_ij - delta_i), per query head h of kv group kv = h / G:
+ *   dq_i   = scale * sum_{j in A_i} dS_ij k_j
+ *   dk_j   = scale * sum_{h in group} sum_{i : j in A_i} dS_ij q_i
+ *   dv_j   =         sum_{h in group} sum_{i : j in A_i} P_ij dout_i
+ * A row with an empty set contributes nothing.  Returns 0, or -1 on bad args.
+ */
+int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void *dout,
+                        int dtype, const int32_t *block_idx,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                        int64_t bs, int64_t S,
+                        const int64_t *qrows, int64_t nq, double *dq,
+                        const int64_t *krows, int64_t nk, double *dk, double *dv,
+                        int nthreads) {
+    if (!q || !k || !v || !dout || !block_idx) return -1;
+    if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || D <= 0 || bs <= 0 || S < 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    const int64_t G = Hq / Hkv, nblk = T / bs;
+    const double scale = 1.0 / sqrt((double)D);
+    if (!qrows) nq = B * Hq * T;
+    if (!krows) nk = B * Hkv * T;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        unsigned char *chosen = (unsigned char *)calloc((size_t)(nblk > 0 ? nblk : 1), 1);
+        if (!chosen) bad = 1;
+        if (dq) {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t n = 0; n < nq; ++n) {
+                if (!chosen) continue;
+                const int64_t r = qrows ? qrows[n] : n;
+                double *o = dq + n * D;
+                for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+                if (r < 0 || r >= B * Hq * T) { bad = 1; continue; }
+                const int64_t bh = r / T, i = r % T, b = bh / Hq, h = bh % Hq, kv = h / G;
+                const int64_t qrow = (bh * T + i) * D, kvslab = (b * Hkv + kv) * T * D;
+                nsa_attended(block_idx + ((b * Hkv + kv) * T + i) * S, S, nblk, bs, i, chosen);
+                double M, l, delta;
+                if (!nsa_row_stats(q, k, v, dout, dtype, chosen, nblk, bs, i, qrow, kvslab, D,
+                                   scale, &M, &l, &delta))
+                    continue;
+                for (int64_t blk = 0; blk < nblk; ++blk) {
+                    if (!chosen[blk]) continue;
+                    for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
+                        double dot = 0.0, dp = 0.0;
+                        for (int64_t d = 0; d < D; ++d) {
+                            dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
+                            dp += widen(dout, dtype, qrow + d) * widen(v, dtype, kvslab + j * D + d);
+                        }
+                        const double P = exp(scale * dot - M) / l;
+                        const double ds = P * (dp - delta);
+                        for (int64_t d = 0; d < D; ++d)
+                            o[d] += scale * ds * widen(k, dtype, kvslab + j * D + d);
+                    }
+                }
+            }
+        }
+        if (dk || dv) {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t n = 0; n < nk; ++n) {
+                if (!chosen) continue;
+                const int64_t r = krows ? krows[n] : n;
+                if (dk) for (int64_t d = 0; d < D; ++d) dk[n * D + d] = 0.0;
+                if (dv) for (int64_t d = 0; d < D; ++d) dv[n * D + d] = 0.0;
+                if (r < 0 || r >= B * Hkv * T) { bad = 1; continue; }
+                const int64_t bkv = r / T, j = r % T, b = bkv / Hkv, kv = bkv % Hkv;
+                const int64_t kvslab = bkv * T * D, blk = j / bs;
+                if (blk >= nblk) continue;
+                for (int64_t i = j; i < T; ++i) {
+                    nsa_attended(block_idx + (bkv * T + i) * S, S, nblk, bs, i, chosen);
+                    if (!chosen[blk]) continue;
+                    for (int64_t g = 0; g < G; ++g) {
+                        const int64_t h = kv * G + g;
+                        const int64_t qrow = ((b * Hq + h) * T + i) * D;
+                        double M, l, delta;
+                        if (!nsa_row_stats(q, k, v, dout, dtype, chosen, nblk, bs, i, qrow,
+                                           kvslab, D, scale, &M, &l, &delta))
+                            continue;
+                        double dot = 0.0, dp = 0.0;
+                        for (int64_t d = 0; d < D; ++d) {
+                            dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
+                            dp += widen(dout, dtype, qrow + d) * widen(v, dtype, kvslab + j * D + d);
+                        }
+                        const double P = exp(scale * dot - M) / l;
+                        const double ds = P * (dp - delta);
+                        for (int64_t d = 0; d < D; ++d) {
+                            if (dk) dk[n * D + d] += scale * ds * widen(q, dtype, qrow + d);
+                            if (dv) dv[n * D + d] += P * widen(dout, dtype, qrow + d);
+                        }
+                    }
+                }
+            }
+        }
+        free(chosen);
     }
     return bad ? -1 : 0;
 }
