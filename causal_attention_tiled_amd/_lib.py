@@ -43,6 +43,10 @@ def load_library():
     lib.tra_fwd.restype = ci
     lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_fwd_f32.restype = ci
+    lib.nsa_sel_bwd.argtypes = [vp] * 10 + [ctypes.c_size_t] + [ci] * 7 + [vp]
+    lib.nsa_sel_bwd.restype = ci
+    lib.nsa_sel_bwd_workspace_bytes.argtypes = [ci] * 7
+    lib.nsa_sel_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.tra_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_bwd.restype = ci
     lib.tda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
@@ -215,3 +219,51 @@ def nsa_sel_fwd(q, k, v, block_idx, block_size, out=None, lse=None, stream=None,
     if rc != 0:
         raise AttnError("nsa_sel_fwd", rc)
     return out, lse
+
+
+def nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, block_size, S) -> int:
+    """Bytes of device workspace nsa_sel_bwd needs."""
+    return int(load_library().nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, block_size, S))
+
+
+def nsa_sel_bwd(q, k, v, block_idx, block_size, lse, dout, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """NSA selection-branch backward (bf16 in / out).
+
+    q, dout: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: int32 [B, Hkv, T, S];
+    lse: fp32 [B, Hq, T] as returned by nsa_sel_fwd.  ``workspace`` (uint8 GPU tensor of
+    at least ``nsa_sel_bwd_workspace_bytes`` bytes) is allocated here when not given.
+    Returns (dq, dk, dv).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(t, n, torch.bfloat16)
+    _check(block_idx, "block_idx", torch.int32)
+    _check(lse, "lse", torch.float32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or dout.shape != q.shape:
+        raise ValueError("q, dout must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, Hkv, T):
+        raise ValueError("block_idx must be [B, Hkv, T, S]")
+    if tuple(lse.shape) != (B, Hq, T):
+        raise ValueError("lse must be [B, Hq, T]")
+    S = block_idx.shape[3]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for g, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _check(g, n, torch.bfloat16)
+        if g.shape != ref.shape:
+            raise ValueError(f"{n} has the wrong shape")
+    if workspace is None:
+        need = nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, block_size, S)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", workspace.dtype)
+    rc = load_library().nsa_sel_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    block_idx.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), B, Hq, Hkv, T,
+                                    D, int(block_size), S, _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("nsa_sel_bwd", rc)
+    return dq, dk, dv

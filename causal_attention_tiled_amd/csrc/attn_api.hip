@@ -34,6 +34,30 @@ int tra_validate(const void *q, const void *k, const void *v, const void *out, i
     return ATTN_OK;
 }
 
+// Shared checks of the NSA selection forward and backward (shapes, sizes, the
+// pointers both read); *noop is set for an empty problem.
+int nsa_validate(const void *q, const void *k, const void *v, const int32_t *block_idx,
+                 int B, int Hq, int Hkv, int T, int D, int block_size, int S, bool *noop) {
+    *noop = false;
+    if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || D < 0 || S < 1 || block_size <= 0)
+        return ATTN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != 32 && block_size != 64 && block_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+    if (S > 64) return ATTN_ERR_UNSUPPORTED;
+    if (T % block_size != 0) return ATTN_ERR_SHAPE;
+    if (B == 0 || Hq == 0 || T == 0) {
+        *noop = true;
+        return ATTN_OK;
+    }
+    if (!q || !k || !v || !block_idx) return ATTN_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v)) return ATTN_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(block_idx) & 3u) != 0) return ATTN_ERR_ALIGN;
+    if (!grid_fits((int64_t)B * Hkv * ((T + 3) / 4))) return ATTN_ERR_SHAPE;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, int B, int H,
@@ -106,24 +130,52 @@ ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const vo
 ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
                             const int32_t *block_idx, void *out, float *lse, int B, int Hq,
                             int Hkv, int T, int D, int block_size, int S, void *stream) {
-    if (B < 0 || Hq < 0 || Hkv <= 0 || T < 0 || D < 0 || S < 1 || block_size <= 0)
-        return ATTN_ERR_SHAPE;
-    if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
-    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-    if (block_size != 32 && block_size != 64 && block_size != 128) return ATTN_ERR_UNSUPPORTED;
-    if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
-    if (S > 64) return ATTN_ERR_UNSUPPORTED;
-    if (T % block_size != 0) return ATTN_ERR_SHAPE;
-    if (B == 0 || Hq == 0 || T == 0) return ATTN_OK;
-    if (!q || !k || !v || !block_idx || !out) return ATTN_ERR_NULL;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return ATTN_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(block_idx) & 3u) != 0) return ATTN_ERR_ALIGN;
+    bool noop;
+    const int st = nsa_validate(q, k, v, block_idx, B, Hq, Hkv, T, D, block_size, S, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if (!out) return ATTN_ERR_NULL;
+    if (misaligned(out)) return ATTN_ERR_ALIGN;
     if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
-    if (!grid_fits((int64_t)B * Hkv * ((T + 3) / 4))) return ATTN_ERR_SHAPE;
     const hipError_t e = attn::launch_nsa_sel_fwd(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), block_idx, static_cast<uint16_t *>(out), lse, B, Hq,
         Hkv, T, D, block_size, S, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+
+ATTN_EXPORT size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D,
+                                               int block_size, int S) {
+    (void)D;
+    if (B <= 0 || Hq <= 0 || T <= 0 || block_size <= 0 || T % block_size != 0 || S < 1 ||
+        Hkv <= 0 || Hq % Hkv != 0)
+        return 0;
+    return attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, block_size, S);
+}
+
+ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
+                            const int32_t *block_idx, const float *lse, const void *dout,
+                            void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int T, int D, int block_size, int S,
+                            void *stream) {
+    bool noop;
+    const int st = nsa_validate(q, k, v, block_idx, B, Hq, Hkv, T, D, block_size, S, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if (!lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+        return ATTN_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
+    // per-batch byte offsets of q / dout rows must fit the 32-bit buffer addressing
+    if ((int64_t)Hq * T * D * 2 >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    const size_t need = attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, block_size, S);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;
+    const hipError_t e = attn::launch_nsa_sel_bwd(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), block_idx, lse, static_cast<const uint16_t *>(dout),
+        static_cast<uint16_t *>(dq),
+        static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), workspace, B, Hq, Hkv, T, D,
+        block_size, S, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

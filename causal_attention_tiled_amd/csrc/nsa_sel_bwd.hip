@@ -1,0 +1,718 @@
+// nsa_sel_bwd.hip -- NSA selection-branch backward for gfx950.
+//
+// The gradients of the selection forward (msb-msb/openbox-llm, page
+// "nsa_selection_kernel.py": module docstring, `selection_forward_reference`,
+// `_selection_fwd_kernel`) with respect to q, k and v; the page keeps the lse
+// output for such a backward but does not show one.  With A_i the attended set of
+// query i (its selected blocks' tokens j <= i, duplicates once), s_ij = scale
+// q_i.k_j, P_ij = exp(s_ij - lse_i), dP_ij = dout_i.v_j, delta_i = sum_j P_ij dP_ij
+// and dS_ij = P_ij (dP_ij - delta_i), for every head h of kv
+// group kv = h / G:
+//     dq_i = scale sum_{j in A_i} dS_ij k_j
+//     dk_j = scale sum_{h, i : j in A_i} dS_ij q_i,   dv_j = sum_{h, i : j in A_i} P_ij dout_i
+//
+// Kernels (all on the caller's stream, workspace from the caller):
+//  * CSR of the selection, inverted: for each (group, block) the increasing list of
+//    queries that attend it.  A bitmap per (group, block) over the query positions
+//    is set with atomic ORs (a repeated slot sets the same bit), its bits are
+//    counted per (group, block), one workgroup scans the counts, and one wave per
+//    (group, block) writes the positions of the set bits in order.  Every step's
+//    result is independent of scheduling.
+//  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
+//    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
+//    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
+//    order, dQ^T += K^T dS^T with K^T read transposed from a per-wave LDS copy of the
+//    chunk.  A first pass over the same chunks sums delta = sum_j P_j dP_j in fp32
+//    (dout . out from the forward's bf16 output is too coarse for dP - delta, which
+//    cancels); the kernel writes delta per (head, query) for the next kernel.
+//  * dk/dv: one workgroup per (group, block), one wavefront per 32 keys of the block
+//    holding its K and V rows in registers, the block's query list walked in chunks
+//    of 32 rows (query, head): their Q and dO rows are gathered into LDS by the
+//    memory unit, with lse, delta and position in a small table.  S = Q K^T and
+//    dP = dO V^T (one key per lane), then dV^T += dO^T P and dK^T += Q^T dS with dO^T
+//    and Q^T read transposed from LDS.  Each key row has one writer: deterministic.
+#include "attn_tile.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kChunk = 32;  // keys per processed chunk in the dq kernel
+constexpr int kDqWaves = 4;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bwd_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void bwd_dma16(__amdgpu_buffer_rsrc_t r, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
+}
+
+// LDS K chunk (32 rows x D*2 bytes) swizzle for the transposing reads (as the
+// forward's V tile): chunk c of row r at slot c ^ swz(r).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int row) {
+    if constexpr (D == 128)
+        return (row & 7) << 1;
+    else
+        return ((row >> 1) & 3) << 1;
+}
+
+// ---------------------------------------------------------------------------
+// CSR build
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// one thread per (group, query, slot): set bit i of the (group, block) bitmap
+__global__ __launch_bounds__(256) void csr_bitmap_kernel(const int32_t *__restrict__ idx,
+                                                         uint32_t *__restrict__ bits, int T,
+                                                         int S, int nblk, int bs, int words,
+                                                         int64_t total) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const int blk = idx[e];
+    const int64_t row = e / S;                // (group, i)
+    const int i = (int)(row % T);
+    const int64_t group = row / T;
+    if (blk < 0 || blk >= nblk || blk * bs > i) return;
+    atomicOr(&bits[(group * nblk + blk) * words + (i >> 5)], 1u << (i & 31));
+}
+
+// one wave per (group, block): number of attending queries
+__global__ __launch_bounds__(256) void csr_count_kernel(const uint32_t *__restrict__ bits,
+                                                        int32_t *__restrict__ counts, int words,
+                                                        int64_t nlists) {
+    const int64_t list = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (list >= nlists) return;
+    const uint32_t *w = bits + list * words;
+    int c = 0;
+    for (int k = lane; k < words; k += 64) c += __builtin_popcount(w[k]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
+    if (lane == 0) counts[list] = c;
+}
+
+// one workgroup: offsets[0] = 0, offsets[k+1] = offsets[k] + counts[k]
+__global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets,
+                                                        int nlists) {
+    __shared__ int32_t part[1024];
+    const int t = threadIdx.x;
+    const int per = (nlists + 1023) / 1024;
+    const int lo = min(t * per, nlists), hi = min(lo + per, nlists);
+    int s = 0;
+    for (int k = lo; k < hi; ++k) s += counts[k];
+    part[t] = s;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan of the per-thread sums
+        const int v = t >= d ? part[t - d] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int run = t > 0 ? part[t - 1] : 0;
+    if (t == 0) offsets[0] = 0;
+    for (int k = lo; k < hi; ++k) {
+        run += counts[k];
+        offsets[k + 1] = run;
+    }
+}
+
+// one wave per (group, block): positions of the set bits, increasing
+__global__ __launch_bounds__(256) void csr_fill_kernel(const uint32_t *__restrict__ bits,
+                                                       const int32_t *__restrict__ offsets,
+                                                       int32_t *__restrict__ list, int words,
+                                                       int64_t nlists) {
+    const int64_t l = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (l >= nlists) return;
+    const uint32_t *w = bits + l * words;
+    int base = offsets[l];
+    for (int k0 = 0; k0 < words; k0 += 64) {
+        const int k = k0 + lane;
+        uint32_t x = k < words ? w[k] : 0u;
+        const int c = __builtin_popcount(x);
+        int incl = c;  // inclusive prefix over the wave
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int y = __shfl_up(incl, m, 64);
+            if (lane >= m) incl += y;
+        }
+        int pos = base + incl - c;
+        while (x) {
+            const int bit = __builtin_ctz(x);
+            x &= x - 1;
+            list[pos++] = k * 32 + bit;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq (query-outer) and delta
+// ---------------------------------------------------------------------------
+
+template <int D, int BS>
+__global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const int32_t *__restrict__ IDX,
+    const float *__restrict__ LSE, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ,
+    float *__restrict__ DELTA,
+    int Hq, int Hkv, int G, int T, int S, int nq4, int ngroups, float score_scale, float scale) {
+    constexpr int ROWB = D * 2;
+    constexpr int NCH = BS / kChunk;
+    constexpr int NDS = D / 32;              // k-steps of S^T and dP^T
+    constexpr int NDT = D / 16;              // 16-dim tiles of dQ^T
+    constexpr int KTILE = kChunk * ROWB;
+    constexpr int KDMA = KTILE / 1024;
+    static_assert(BS % kChunk == 0 && KTILE % 1024 == 0, "chunking");
+
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf_a[kDqWaves][KTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf_b[kDqWaves][KTILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n16 = lane & 15, g4 = lane >> 4;
+    const int W = ngroups * nq4;
+    int f = blockIdx.x;
+    if ((W & 7) == 0) f = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
+    const int group = __builtin_amdgcn_readfirstlane(f / nq4);
+    const int i = __builtin_amdgcn_readfirstlane((nq4 - 1 - f % nq4) * kDqWaves + wave);
+    if (i >= T) return;  // no workgroup-wide barrier in this kernel
+    const int b = group / Hkv, kv = group % Hkv;
+    const size_t kvslab = (size_t)group * T * D;
+    const __amdgpu_buffer_rsrc_t rk = bwd_rsrc(K + kvslab, (uint32_t)T * ROWB);
+    const __amdgpu_buffer_rsrc_t rv = bwd_rsrc(V + kvslab, (uint32_t)T * ROWB);
+
+    const int nblk = T / BS;
+    const int32_t *slots = IDX + ((size_t)group * T + i) * S;
+    const int myblk = lane < S ? slots[lane] : -1;
+    bool keep = myblk >= 0 && myblk < nblk && myblk * BS <= i;
+    for (int s2 = 0; s2 < S; ++s2) {
+        const int other = __builtin_amdgcn_readlane(myblk, s2);
+        keep = keep && !(s2 < lane && other == myblk);
+    }
+    uint64_t rem = __builtin_amdgcn_ballot_w64(keep);
+
+    // Q^T and dO^T operands: head kv*G + n16 (zero for n16 >= G), dims 32*ds + 8*g4 .. +7
+    const bool head_ok = n16 < G;
+    const int head = kv * G + (head_ok ? n16 : 0);
+    const size_t qrow = ((size_t)(b * Hq + head) * T + i) * D;
+    bf16x8 qf[NDS], df[NDS];
+    {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 a = z, c = z;
+            if (head_ok) {
+                a = *(const u32x4 *)(Q + qrow + ds * 32 + g4 * 8);
+                c = *(const u32x4 *)(dO + qrow + ds * 32 + g4 * 8);
+            }
+            qf[ds] = as_bf16x8(a);
+            df[ds] = as_bf16x8(c);
+        }
+    }
+    const float lse2 = head_ok ? LSE[(size_t)(b * Hq + head) * T + i] * kLog2e : 0.0f;
+
+    const int koff = n16 * ROWB + g4 * 16;  // K or V row 16*kk + n16, dims 32*ds + 8*g4
+    int kdma_off[KDMA];
+#pragma unroll
+    for (int j = 0; j < KDMA; ++j) {
+        const int pos = j * 1024 + lane * 16;
+        const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
+        kdma_off[j] = row * ROWB + ((slot ^ chunk_swz<D>(row)) << 4);
+    }
+    // K^T operand reads: rows 4*g4 + s/4 (+16), dims 16*dt + 4*(s%4)
+    int krd_off[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = 4 * g4 + (n16 >> 2) + 16 * h;
+            const int col = 16 * dt + 4 * (n16 & 3);
+            krd_off[dt][h] = row * ROWB + (((col >> 3) ^ chunk_swz<D>(row)) << 4) + (col & 7) * 2;
+        }
+
+    typedef uint8_t KTileBuf[kDqWaves][KTILE];
+    bf16x8 kfa[2][NDS], vfa[2][NDS], kfb[2][NDS], vfb[2][NDS];
+    auto load_rows = [&](int k0, bf16x8 (&kf)[2][NDS], bf16x8 (&vf)[2][NDS]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                kf[kk][ds] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + ds * 64,
+                                                                  (k0 + 16 * kk) * ROWB, 0));
+                vf[kk][ds] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, koff + ds * 64,
+                                                                  (k0 + 16 * kk) * ROWB, 0));
+            }
+    };
+    auto load_chunk = [&](int k0, bf16x8 (&kf)[2][NDS], bf16x8 (&vf)[2][NDS], KTileBuf &kt) {
+        load_rows(k0, kf, vf);
+#pragma unroll
+        for (int j = 0; j < KDMA; ++j) bwd_dma16(rk, &kt[wave][j * 1024], kdma_off[j], k0 * ROWB);
+    };
+    // S^T and dP^T of one chunk: register j of st[kk] / dp[kk] is key k0 + 16*kk + 4*g4 + j,
+    // head n16; returns the probabilities (0 for keys after i) in pr
+    auto scores = [&](int k0, const bf16x8 (&kf)[2][NDS], const bf16x8 (&vf)[2][NDS],
+                      f32x4 (&pr)[2], f32x4 (&dp)[2]) {
+        f32x4 st[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            st[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            dp[kk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                st[kk] = mfma_16x16x32(kf[kk][ds], qf[ds], st[kk]);
+                dp[kk] = mfma_16x16x32(vf[kk][ds], df[ds], dp[kk]);
+            }
+        }
+        const int lim = i - k0 - 4 * g4;  // key offset 16*kk + j is attended iff <= lim
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float e = __builtin_amdgcn_exp2f(st[kk][j] * score_scale - lse2);
+                pr[kk][j] = 16 * kk + j > lim ? 0.0f : e;
+            }
+    };
+
+    f32x4 dqacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    float delta = 0.0f;
+    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const bf16x8 (&vf)[2][NDS],
+                             const KTileBuf &kt) {
+        f32x4 pr[2], dp[2];
+        scores(k0, kf, vf, pr, dp);
+        bf16x8 pf;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - delta));
+        // dQ^T += K^T dS^T : register j of dqacc[dt] is dim 16*dt + 4*g4 + j, head n16
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const uint8_t *base = &kt[wave][0];
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4 *)(base + krd_off[dt][0]));
+            const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4 *)(base + krd_off[dt][1]));
+            dqacc[dt] = mfma_16x16x32(__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7), pf,
+                                      dqacc[dt]);
+        }
+    };
+
+    int cur_blk = -1, cur_c = 0;
+    auto next_chunk = [&]() -> int {
+        if (cur_blk >= 0 && cur_c + 1 < NCH && cur_blk * BS + (cur_c + 1) * kChunk <= i) {
+            ++cur_c;
+            return cur_blk * BS + cur_c * kChunk;
+        }
+        if (rem == 0) return -1;
+        const int s = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        cur_blk = __builtin_amdgcn_readlane(myblk, s);
+        cur_c = 0;
+        return cur_blk * BS;
+    };
+
+    // Pass 1: delta = sum_j P_j dP_j over the attended keys, in fp32 from the scores
+    // (the forward's bf16 output is too coarse for dP - delta, which cancels).
+    const uint64_t rem0 = rem;
+    {
+        float dl = 0.0f;
+        int ka = next_chunk();
+        if (ka >= 0) load_rows(ka, kfa, vfa);
+        while (ka >= 0) {
+            const int kb = next_chunk();
+            if (kb >= 0) load_rows(kb, kfb, vfb);
+            f32x4 pr[2], dp[2];
+            scores(ka, kfa, vfa, pr, dp);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dl = fmaf(pr[kk][j], dp[kk][j], dl);
+            if (kb < 0) break;
+            ka = next_chunk();
+            if (ka >= 0) load_rows(ka, kfa, vfa);
+            scores(kb, kfb, vfb, pr, dp);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dl = fmaf(pr[kk][j], dp[kk][j], dl);
+        }
+        dl += __shfl_xor(dl, 16);
+        dl += __shfl_xor(dl, 32);
+        delta = dl;
+        if (head_ok && g4 == 0) DELTA[(size_t)(b * Hq + head) * T + i] = delta;
+    }
+    // Pass 2: dS and dQ
+    rem = rem0;
+    cur_blk = -1;
+    cur_c = 0;
+    int ka = next_chunk();
+    if (ka >= 0) load_chunk(ka, kfa, vfa, kbuf_a);
+    int kb = ka >= 0 ? next_chunk() : -1;
+    while (ka >= 0) {
+        if (kb >= 0) load_chunk(kb, kfb, vfb, kbuf_b);
+        compute_chunk(ka, kfa, vfa, kbuf_a);
+        if (kb < 0) break;
+        ka = next_chunk();
+        if (ka >= 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of kbuf_a done
+            load_chunk(ka, kfa, vfa, kbuf_a);
+        }
+        compute_chunk(kb, kfb, vfb, kbuf_b);
+        kb = ka >= 0 ? next_chunk() : -1;
+        if (kb >= 0) __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+
+    if (head_ok) {
+        uint16_t *row = dQ + qrow;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const u32x2 pr = {pack_bf16x2(scale * dqacc[dt][0], scale * dqacc[dt][1]),
+                              pack_bf16x2(scale * dqacc[dt][2], scale * dqacc[dt][3])};
+            *(u32x2 *)(row + dt * 16 + g4 * 4) = pr;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dk / dv (block-outer over the inverted CSR)
+// ---------------------------------------------------------------------------
+
+template <int D, int BS>
+__global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, const float *__restrict__ DELTA,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ list,
+    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int Hq, int Hkv, int G, int T,
+    int nblk, float score_scale, float scale) {
+    constexpr int NW = BS / 32;                  // one wave per 32 keys of the block
+    constexpr int ROWB = D * 2;
+    constexpr int CH = D / 8;
+    constexpr int TILEB = 32 * ROWB;             // 32 gathered rows of one tensor
+    constexpr int LOADS = 32 * CH / (64 * NW);   // 16-byte chunks per lane per tensor
+    constexpr int NDS = D / 16;
+    constexpr int NDT = D / 32;
+    constexpr int QB = 0, OB = 2 * TILEB;        // Q rows (2 buffers), then dO rows
+    static_assert(LOADS >= 1 && 32 * CH % (64 * NW) == 0, "row staging");
+
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TILEB];
+    // per staged row: lse' (base 2), delta, query position (-1: no row)
+    __shared__ __attribute__((aligned(16))) float rlse[2][32];
+    __shared__ __attribute__((aligned(16))) float rdelta[2][32];
+    __shared__ __attribute__((aligned(16))) int rpos[2][32];
+
+    // workgroup -> (group, block); blocks with the most attending queries (small ids)
+    // first, groups spread over the XCDs
+    const int ngroups = gridDim.x / nblk;
+    int group, blk;
+    if ((ngroups & 7) == 0) {
+        const int bid = blockIdx.x, xcd = bid & 7, s = bid >> 3, gpx = ngroups >> 3;
+        group = xcd * gpx + s % gpx;
+        blk = s / gpx;
+    } else {
+        group = blockIdx.x % ngroups;
+        blk = blockIdx.x / ngroups;
+    }
+    group = __builtin_amdgcn_readfirstlane(group);
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    const int b = group / Hkv, kv = group % Hkv;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5;
+    const size_t kvslab = (size_t)group * T * D;
+    const int kw0 = blk * BS + 32 * wave;        // this wave's keys
+    const int mykey = kw0 + l32;
+
+    const int lbeg = offsets[group * nblk + blk];
+    const int nq = offsets[group * nblk + blk + 1] - lbeg;
+    const int32_t *qlist = list + lbeg;
+    const int qc = 32 / G;                       // queries per chunk of rows
+    const int rows_used = qc * G;
+    const int nchunks = (nq + qc - 1) / qc;
+
+    // Q and dO of batch b: rows (h, i) at ((h*T + i) * ROWB)
+    const size_t bslab = (size_t)b * Hq * T * D;
+    const uint32_t bbytes = (uint32_t)((size_t)Hq * T * ROWB);
+    const __amdgpu_buffer_rsrc_t rq = bwd_rsrc(Q + bslab, bbytes);
+    const __amdgpu_buffer_rsrc_t ro = bwd_rsrc(dO + bslab, bbytes);
+
+    // staging positions: DMA instruction j of wave w fills tile bytes
+    // [(w*LOADS + j)*1024, +1024); lane l the 16 bytes at +16*l, i.e. row r = pos / ROWB
+    // and chunk slot; it fetches chunk slot ^ swz(r) of that row's source
+    int srow[LOADS], sslot[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int pos = (wave * LOADS + j) * 1024 + lane * 16;
+        srow[j] = pos / ROWB;
+        sslot[j] = ((pos % ROWB) >> 4) ^ tile_swz<D>(pos / ROWB);
+    }
+    auto stage = [&](int c, int buf) {
+        // row r of chunk c: query qlist[c*qc + r/G], head kv*G + r%G
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int r = srow[j];
+            const int qi = c * qc + r / G;
+            int off = (int)bbytes;  // past the end: reads zero
+            if (r < rows_used && qi < nq) {
+                const int h = kv * G + r % G;
+                off = (h * T + qlist[qi]) * ROWB + (sslot[j] << 4);
+            }
+            const int dst = buf * TILEB + (wave * LOADS + j) * 1024;
+            bwd_dma16(rq, &lds[QB + dst], off, 0);
+            bwd_dma16(ro, &lds[OB + dst], off, 0);
+        }
+        if (wave == 0 && lane < 32) {
+            const int qi = c * qc + lane / G;
+            float ls = INFINITY, de = 0.0f;
+            int pos = -1;
+            if (lane < rows_used && qi < nq) {
+                const int h = kv * G + lane % G;
+                pos = qlist[qi];
+                const size_t rowid = (size_t)(b * Hq + h) * T + pos;
+                ls = LSE[rowid] * kLog2e;
+                de = DELTA[rowid];
+            }
+            rlse[buf][lane] = ls;
+            rdelta[buf][lane] = de;
+            rpos[buf][lane] = pos;
+        }
+    };
+
+    int roff[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) roff[ds] = l32 * ROWB + (((2 * ds + hi) ^ tile_swz<D>(l32)) << 4);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int trow = 4 * (g16 >> 1) + (s16 >> 2);
+    int toff[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = trow + 8 * h;
+            toff[dt][h] = row * ROWB +
+                          (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
+                          8 * (s16 & 1);
+        }
+    auto row_frag = [&](int base, int buf, int ds) {
+        return *(const bf16x8 *)(&lds[roff[ds] + base + buf * TILEB]);
+    };
+    auto t_frag = [&](int base, int buf, int dt, int c) {
+        const uint8_t *p = &lds[base + buf * TILEB + 16 * c * ROWB];
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][0]));
+        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][1]));
+        return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x16 dkacc[NDT], dvacc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[dt][r] = dvacc[dt][r] = 0.0f;
+
+    if (nchunks > 0) stage(0, 0);
+    bf16x8 kf[NDS], vf[NDS];
+    {
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 a = zero4, c = zero4;
+            if (mykey < T) {
+                a = *(const u32x4 *)(K + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
+                c = *(const u32x4 *)(V + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
+            }
+            kf[ds] = as_bf16x8(a);
+            vf[ds] = as_bf16x8(c);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+
+    f32x16 zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < nchunks) stage(c + 1, buf ^ 1);
+        // register r: row m = 8*(r/4) + 4*hi + r%4 of the chunk, key mykey (lane)
+        f32x16 s = zero16, dp = zero16;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            s = mfma_32x32x16(row_frag(QB, buf, ds), kf[ds], s);
+            dp = mfma_32x32x16(row_frag(OB, buf, ds), vf[ds], dp);
+        }
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 ls = *(const f32x4 *)(&rlse[buf][8 * g + 4 * hi]);
+            const f32x4 de = *(const f32x4 *)(&rdelta[buf][8 * g + 4 * hi]);
+            const i32x4 ps = *(const i32x4 *)(&rpos[buf][8 * g + 4 * hi]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g + j;
+                float pr = __builtin_amdgcn_exp2f(s[r] * score_scale - ls[j]);
+                if (mykey > ps[j]) pr = 0.0f;  // after the query (or no row: ps = -1)
+                pb[r >> 3][r & 7] = (__bf16)pr;
+                sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - de[j]));
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                dvacc[dt] = mfma_32x32x16(t_frag(OB, buf, dt, cc), pb[cc], dvacc[dt]);
+                dkacc[dt] = mfma_32x32x16(t_frag(QB, buf, dt, cc), sb[cc], dkacc[dt]);
+            }
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_barrier();
+    }
+
+    if (mykey < T) {
+        uint16_t *krow = dK + kvslab + (size_t)mykey * D;
+        uint16_t *vrow = dV + kvslab + (size_t)mykey * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const u32x2 kp = {pack_bf16x2(scale * dkacc[dt][4 * i4], scale * dkacc[dt][4 * i4 + 1]),
+                                  pack_bf16x2(scale * dkacc[dt][4 * i4 + 2], scale * dkacc[dt][4 * i4 + 3])};
+                const u32x2 vp = {pack_bf16x2(dvacc[dt][4 * i4], dvacc[dt][4 * i4 + 1]),
+                                  pack_bf16x2(dvacc[dt][4 * i4 + 2], dvacc[dt][4 * i4 + 3])};
+                *(u32x2 *)(krow + dt * 32 + 8 * i4 + 4 * hi) = kp;
+                *(u32x2 *)(vrow + dt * 32 + 8 * i4 + 4 * hi) = vp;
+            }
+    }
+}
+
+// Workspace layout (all 256-byte aligned): bitmap, counts, offsets, list, delta.
+struct BwdLayout {
+    size_t bits, counts, offsets, list, delta, total;
+};
+
+BwdLayout layout(int B, int Hq, int Hkv, int T, int bs, int S) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t nlists = (size_t)B * Hkv * (T / bs);
+    const size_t words = ((size_t)T + 31) / 32;
+    BwdLayout L;
+    L.bits = 0;
+    L.counts = al(L.bits + nlists * words * 4);
+    L.offsets = al(L.counts + nlists * 4);
+    L.list = al(L.offsets + (nlists + 1) * 4);
+    L.delta = al(L.list + (size_t)B * Hkv * T * S * 4);
+    L.total = al(L.delta + (size_t)B * Hq * T * 4);
+    return L;
+}
+
+template <int D, int BS>
+hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *idx,
+                  const float *lse, const uint16_t *dout, uint16_t *dq,
+                  uint16_t *dk, uint16_t *dv, uint8_t *ws, int B, int Hq, int Hkv, int T, int S,
+                  hipStream_t stream) {
+    const BwdLayout L = layout(B, Hq, Hkv, T, BS, S);
+    uint32_t *bits = (uint32_t *)(ws + L.bits);
+    int32_t *counts = (int32_t *)(ws + L.counts);
+    int32_t *offsets = (int32_t *)(ws + L.offsets);
+    int32_t *list = (int32_t *)(ws + L.list);
+    float *delta = (float *)(ws + L.delta);
+    int nblk = T / BS;
+    int words = (T + 31) / 32;
+    int64_t nlists = (int64_t)B * Hkv * nblk;
+    int G = Hq / Hkv;
+    float score_scale = kLog2e / sqrtf((float)D);
+    float scale = 1.0f / sqrtf((float)D);
+    hipError_t e;
+    {
+        int64_t n = nlists * words;
+        void *a[] = {&bits, &n};
+        e = hipLaunchKernel((const void *)fill_u32_kernel, dim3((unsigned)((n + 255) / 256)),
+                            dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        int64_t total = (int64_t)B * Hkv * T * S;
+        int bs = BS;
+        void *a[] = {&idx, &bits, &T, &S, &nblk, &bs, &words, &total};
+        e = hipLaunchKernel((const void *)csr_bitmap_kernel, dim3((unsigned)((total + 255) / 256)),
+                            dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&bits, &counts, &words, &nlists};
+        e = hipLaunchKernel((const void *)csr_count_kernel, dim3((unsigned)((nlists + 3) / 4)),
+                            dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        int n = (int)nlists;
+        void *a[] = {&counts, &offsets, &n};
+        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&bits, &offsets, &list, &words, &nlists};
+        e = hipLaunchKernel((const void *)csr_fill_kernel, dim3((unsigned)((nlists + 3) / 4)),
+                            dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        int nq4 = (T + kDqWaves - 1) / kDqWaves;
+        int ngroups = B * Hkv;
+        void *a[] = {&q, &k, &v, &idx, &lse, &dout, &dq, &delta, &Hq, &Hkv, &G, &T, &S,
+                     &nq4, &ngroups, &score_scale, &scale};
+        e = hipLaunchKernel((const void *)nsa_bwd_dq_kernel<D, BS>,
+                            dim3((unsigned)(ngroups * nq4)), dim3(64 * kDqWaves), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&q, &k, &v, &lse, &dout, &delta, &offsets, &list, &dk, &dv, &Hq, &Hkv, &G,
+                     &T, &nblk, &score_scale, &scale};
+        return hipLaunchKernel((const void *)nsa_bwd_dkv_kernel<D, BS>,
+                               dim3((unsigned)nlists), dim3(64 * (BS / 32)), a, 0, stream);
+    }
+}
+
+}  // namespace
+
+size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int block_size, int S) {
+    return layout(B, Hq, Hkv, T, block_size, S).total;
+}
+
+hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *block_idx, const float *lse, const uint16_t *dout,
+                              uint16_t *dq, uint16_t *dk, uint16_t *dv, void *workspace, int B,
+                              int Hq, int Hkv, int T, int D, int block_size, int S,
+                              hipStream_t stream) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+#define ATTN_NSA_BWD_CASE(DD, BB)                                                            \
+    if (D == DD && block_size == BB)                                                        \
+        return launch<DD, BB>(q, k, v, block_idx, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, \
+                              stream);
+    ATTN_NSA_BWD_CASE(128, 64)
+    ATTN_NSA_BWD_CASE(128, 32)
+    ATTN_NSA_BWD_CASE(128, 128)
+    ATTN_NSA_BWD_CASE(64, 64)
+    ATTN_NSA_BWD_CASE(64, 32)
+    ATTN_NSA_BWD_CASE(64, 128)
+#undef ATTN_NSA_BWD_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

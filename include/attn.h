@@ -182,6 +182,49 @@ int nsa_sel_fwd(const void *q, const void *k, const void *v, const int32_t *bloc
                 void *out, float *lse,
                 int B, int Hq, int Hkv, int T, int D, int block_size, int S, void *stream);
 
+/*
+ * NSA selection-branch backward, bf16 in / bf16 out.
+ *
+ * Source: msb-msb/openbox-llm, page "nsa_selection_kernel.py" -- the forward
+ * above defines the function; the page keeps its lse output for a backward
+ * pass that it does not show.  These are the gradients of that forward with
+ * respect to q, k and v (block_idx is an integer index and gets none).
+ *
+ * With A_i the attended set of query i (as in the forward), s_ij = (q_i . k_j)
+ * / sqrt(D), P_ij = exp(s_ij - lse_i), dP_ij = dout_i . v_j, delta_i =
+ * sum_{j in A_i} P_ij dP_ij and dS_ij = P_ij (dP_ij - delta_i), for each head h
+ * of kv group kv:
+ *   dq_i = sum_{j in A_i} dS_ij k_j / sqrt(D)
+ *   dk_j = sum_{h in group, i : j in A_i} dS_ij q_i / sqrt(D)
+ *   dv_j = sum_{h in group, i : j in A_i} P_ij dout_i
+ *
+ *   q, dout      : bf16 [B, Hq, T, D]
+ *   k, v         : bf16 [B, Hkv, T, D]
+ *   block_idx    : int32 [B, Hkv, T, S]
+ *   lse          : fp32 [B, Hq, T]      (as returned by nsa_sel_fwd)
+ *   dq           : bf16 [B, Hq, T, D]   (written)
+ *   dk, dv       : bf16 [B, Hkv, T, D]  (written; a key row no query attends gets 0)
+ *   workspace    : device memory the call overwrites, at least
+ *                  nsa_sel_bwd_workspace_bytes(...) bytes, 256-byte aligned (else
+ *                  ATTN_ERR_WORKSPACE / ATTN_ERR_ALIGN).  Calls that share one
+ *                  workspace must not overlap in time.
+ *   sizes        : as nsa_sel_fwd; in addition Hq*T*D*2 < 2^31 (else
+ *                  ATTN_ERR_UNSUPPORTED).
+ *
+ * Numerics: scores, dP and delta in fp32 from bf16 products (delta from the
+ * recomputed probabilities, not from the forward's rounded output); P and dS
+ * rounded to bf16 before the products that consume them; fp32 accumulation;
+ * every gradient row has one writer (no atomics on values): deterministic.
+ */
+int nsa_sel_bwd(const void *q, const void *k, const void *v, const int32_t *block_idx,
+                const float *lse, const void *dout,
+                void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                int B, int Hq, int Hkv, int T, int D, int block_size, int S, void *stream);
+
+/* Workspace bytes nsa_sel_bwd needs for these sizes (0 if a size is invalid or
+ * the problem is empty). */
+size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *attn_status_str(int status);
 
