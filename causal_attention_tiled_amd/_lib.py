@@ -43,7 +43,7 @@ def load_library():
     lib.tra_fwd.restype = ci
     lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_fwd_f32.restype = ci
-    lib.nsa_sel_bwd.argtypes = [vp] * 10 + [ctypes.c_size_t] + [ci] * 7 + [vp]
+    lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 7 + [vp]
     lib.nsa_sel_bwd.restype = ci
     lib.nsa_sel_bwd_workspace_bytes.argtypes = [ci] * 7
     lib.nsa_sel_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -226,21 +226,22 @@ def nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, block_size, S) -> int:
     return int(load_library().nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, block_size, S))
 
 
-def nsa_sel_bwd(q, k, v, block_idx, block_size, lse, dout, dq=None, dk=None, dv=None,
+def nsa_sel_bwd(q, k, v, block_idx, block_size, out, lse, dout, dq=None, dk=None, dv=None,
                 workspace=None, stream=None):
     """NSA selection-branch backward (bf16 in / out).
 
-    q, dout: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: int32 [B, Hkv, T, S];
-    lse: fp32 [B, Hq, T] as returned by nsa_sel_fwd.  ``workspace`` (uint8 GPU tensor of
-    at least ``nsa_sel_bwd_workspace_bytes`` bytes) is allocated here when not given.
-    Returns (dq, dk, dv).
+    q, out, dout: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; block_idx: int32 [B, Hkv, T, S];
+    lse: fp32 [B, Hq, T] (out and lse as returned by nsa_sel_fwd).  ``workspace`` (uint8
+    GPU tensor of at least ``nsa_sel_bwd_workspace_bytes`` bytes) is allocated here when
+    not given.  Returns (dq, dk, dv).
     """
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
         _check(t, n, torch.bfloat16)
     _check(block_idx, "block_idx", torch.int32)
     _check(lse, "lse", torch.float32)
-    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or dout.shape != q.shape:
-        raise ValueError("q, dout must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or out.shape != q.shape \
+            or dout.shape != q.shape:
+        raise ValueError("q, out, dout must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     if block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, Hkv, T):
@@ -260,7 +261,8 @@ def nsa_sel_bwd(q, k, v, block_idx, block_size, lse, dout, dq=None, dk=None, dv=
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(workspace, "workspace", workspace.dtype)
     rc = load_library().nsa_sel_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                    block_idx.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    block_idx.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                     workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), B, Hq, Hkv, T,
                                     D, int(block_size), S, _stream_handle(stream))

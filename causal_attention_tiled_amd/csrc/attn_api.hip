@@ -154,15 +154,15 @@ ATTN_EXPORT size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, in
 }
 
 ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
-                            const int32_t *block_idx, const float *lse, const void *dout,
-                            void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
-                            int B, int Hq, int Hkv, int T, int D, int block_size, int S,
-                            void *stream) {
+                            const int32_t *block_idx, const void *out, const float *lse,
+                            const void *dout, void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
+                            int block_size, int S, void *stream) {
     bool noop;
     const int st = nsa_validate(q, k, v, block_idx, B, Hq, Hkv, T, D, block_size, S, &noop);
     if (st != ATTN_OK || noop) return st;
-    if (!lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
-    if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
+    if (!out || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    if (misaligned(out) || misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv))
         return ATTN_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
     // per-batch byte offsets of q / dout rows must fit the 32-bit buffer addressing
@@ -172,8 +172,8 @@ ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;
     const hipError_t e = attn::launch_nsa_sel_bwd(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-        static_cast<const uint16_t *>(v), block_idx, lse, static_cast<const uint16_t *>(dout),
-        static_cast<uint16_t *>(dq),
+        static_cast<const uint16_t *>(v), block_idx, static_cast<const uint16_t *>(out), lse,
+        static_cast<const uint16_t *>(dout), static_cast<uint16_t *>(dq),
         static_cast<uint16_t *>(dk), static_cast<uint16_t *>(dv), workspace, B, Hq, Hkv, T, D,
         block_size, S, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;

@@ -65,10 +65,10 @@ hipError_t launch_tra_bwd_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
                                int BH, int T, int D, float beta, float p, hipStream_t stream);
 hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                              const int32_t *block_idx, const float *lse, const uint16_t *dout,
-                              uint16_t *dq, uint16_t *dk, uint16_t *dv, void *workspace, int B,
-                              int Hq, int Hkv, int T, int D, int block_size, int S,
-                              hipStream_t stream);
+                              const int32_t *block_idx, const uint16_t *out, const float *lse,
+                              const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                              void *workspace, int B, int Hq, int Hkv, int T, int D,
+                              int block_size, int S, hipStream_t stream);
 // Workspace bytes of the NSA selection backward (block lists, per-row delta).
 size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int block_size, int S);
 hipError_t launch_tda_fwd_bf16(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,

@@ -21,10 +21,15 @@
 //  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
-//    order, dQ^T += K^T dS^T with K^T read transposed from a per-wave LDS copy of the
-//    chunk.  A first pass over the same chunks sums delta = sum_j P_j dP_j in fp32
-//    (dout . out from the forward's bf16 output is too coarse for dP - delta, which
-//    cancels); the kernel writes delta per (head, query) for the next kernel.
+//    order, and dQ^T += K^T (.)^T with K^T read transposed from a per-wave LDS copy
+//    of the chunk.  delta is needed before the first dS and is only known after the
+//    last key, and dout . out from the forward's bf16 output is too coarse a value for
+//    dP - delta, which cancels.  So one pass accumulates, against the estimate
+//    m = dout . out, X = sum_j bf16(P_j (dP_j - m)) k_j, Y = sum_j bf16(P_j) k_j and
+//    delta = sum_j P_j dP_j in fp32, and ends with dq = scale (X - (delta - m) Y): the
+//    correction term is small, so its bf16 operand costs nothing, and the rounding
+//    of the main term is the rounding of dS itself.  The kernel writes delta per
+//    (head, query) for the next kernel.
 //  * dk/dv: one workgroup per (group, block), one wavefront per 32 keys of the block
 //    holding its K and V rows in registers, the block's query list walked in chunks
 //    of 32 rows (query, head): their Q and dO rows are gathered into LDS by the
@@ -165,8 +170,8 @@ template <int D, int BS>
 __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ IDX,
-    const float *__restrict__ LSE, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ,
-    float *__restrict__ DELTA,
+    const uint16_t *__restrict__ O, const float *__restrict__ LSE,
+    const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ, float *__restrict__ DELTA,
     int Hq, int Hkv, int G, int T, int S, int nq4, int ngroups, float score_scale, float scale) {
     constexpr int ROWB = D * 2;
     constexpr int NCH = BS / kChunk;
@@ -209,18 +214,25 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     const int head = kv * G + (head_ok ? n16 : 0);
     const size_t qrow = ((size_t)(b * Hq + head) * T + i) * D;
     bf16x8 qf[NDS], df[NDS];
+    float m = 0.0f;  // dout . out of head n16, the estimate of delta
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-            u32x4 a = z, c = z;
+            u32x4 a = z, c = z, o = z;
             if (head_ok) {
                 a = *(const u32x4 *)(Q + qrow + ds * 32 + g4 * 8);
                 c = *(const u32x4 *)(dO + qrow + ds * 32 + g4 * 8);
+                o = *(const u32x4 *)(O + qrow + ds * 32 + g4 * 8);
             }
             qf[ds] = as_bf16x8(a);
             df[ds] = as_bf16x8(c);
+            const bf16x8 of = as_bf16x8(o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaf((float)df[ds][e], (float)of[e], m);
         }
+        m += __shfl_xor(m, 16);
+        m += __shfl_xor(m, 32);
     }
     const float lse2 = head_ok ? LSE[(size_t)(b * Hq + head) * T + i] * kLog2e : 0.0f;
 
@@ -288,21 +300,29 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
             }
     };
 
-    f32x4 dqacc[NDT];
+    // register j of xacc[dt] / yacc[dt] is dim 16*dt + 4*g4 + j, head n16
+    f32x4 xacc[NDT], yacc[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int dt = 0; dt < NDT; ++dt) {
+        xacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        yacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
-    float delta = 0.0f;
+    float dl = 0.0f;  // this lane's part of delta
     auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const bf16x8 (&vf)[2][NDS],
                              const KTileBuf &kt) {
         f32x4 pr[2], dp[2];
         scores(k0, kf, vf, pr, dp);
-        bf16x8 pf;
+        bf16x8 xf, yf;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - delta));
-        // dQ^T += K^T dS^T : register j of dqacc[dt] is dim 16*dt + 4*g4 + j, head n16
+            for (int j = 0; j < 4; ++j) {
+                dl = fmaf(pr[kk][j], dp[kk][j], dl);
+                xf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - m));
+                yf[kk * 4 + j] = (__bf16)pr[kk][j];
+            }
+        // X^T += K^T xf^T, Y^T += K^T yf^T
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
             const uint8_t *base = &kt[wave][0];
@@ -310,8 +330,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
                 (lds_bf16x4 *)(base + krd_off[dt][0]));
             const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (lds_bf16x4 *)(base + krd_off[dt][1]));
-            dqacc[dt] = mfma_16x16x32(__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7), pf,
-                                      dqacc[dt]);
+            const bf16x8 kt8 = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+            xacc[dt] = mfma_16x16x32(kt8, xf, xacc[dt]);
+            yacc[dt] = mfma_16x16x32(kt8, yf, yacc[dt]);
         }
     };
 
@@ -329,40 +350,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         return cur_blk * BS;
     };
 
-    // Pass 1: delta = sum_j P_j dP_j over the attended keys, in fp32 from the scores
-    // (the forward's bf16 output is too coarse for dP - delta, which cancels).
-    const uint64_t rem0 = rem;
-    {
-        float dl = 0.0f;
-        int ka = next_chunk();
-        if (ka >= 0) load_rows(ka, kfa, vfa);
-        while (ka >= 0) {
-            const int kb = next_chunk();
-            if (kb >= 0) load_rows(kb, kfb, vfb);
-            f32x4 pr[2], dp[2];
-            scores(ka, kfa, vfa, pr, dp);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dl = fmaf(pr[kk][j], dp[kk][j], dl);
-            if (kb < 0) break;
-            ka = next_chunk();
-            if (ka >= 0) load_rows(ka, kfa, vfa);
-            scores(kb, kfb, vfb, pr, dp);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dl = fmaf(pr[kk][j], dp[kk][j], dl);
-        }
-        dl += __shfl_xor(dl, 16);
-        dl += __shfl_xor(dl, 32);
-        delta = dl;
-        if (head_ok && g4 == 0) DELTA[(size_t)(b * Hq + head) * T + i] = delta;
-    }
-    // Pass 2: dS and dQ
-    rem = rem0;
-    cur_blk = -1;
-    cur_c = 0;
     int ka = next_chunk();
     if (ka >= 0) load_chunk(ka, kfa, vfa, kbuf_a);
     int kb = ka >= 0 ? next_chunk() : -1;
@@ -380,13 +367,19 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         if (kb >= 0) __builtin_amdgcn_s_waitcnt(0xC07F);
     }
 
+    dl += __shfl_xor(dl, 16);
+    dl += __shfl_xor(dl, 32);
+    const float corr = dl - m;
     if (head_ok) {
+        if (g4 == 0) DELTA[(size_t)(b * Hq + head) * T + i] = dl;
         uint16_t *row = dQ + qrow;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const u32x2 pr = {pack_bf16x2(scale * dqacc[dt][0], scale * dqacc[dt][1]),
-                              pack_bf16x2(scale * dqacc[dt][2], scale * dqacc[dt][3])};
-            *(u32x2 *)(row + dt * 16 + g4 * 4) = pr;
+            f32x4 r;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = scale * fmaf(-corr, yacc[dt][j], xacc[dt][j]);
+            const u32x2 pk = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+            *(u32x2 *)(row + dt * 16 + g4 * 4) = pk;
         }
     }
 }
@@ -623,7 +616,7 @@ BwdLayout layout(int B, int Hq, int Hkv, int T, int bs, int S) {
 
 template <int D, int BS>
 hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const int32_t *idx,
-                  const float *lse, const uint16_t *dout, uint16_t *dq,
+                  const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
                   uint16_t *dk, uint16_t *dv, uint8_t *ws, int B, int Hq, int Hkv, int T, int S,
                   hipStream_t stream) {
     const BwdLayout L = layout(B, Hq, Hkv, T, BS, S);
@@ -675,7 +668,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     {
         int nq4 = (T + kDqWaves - 1) / kDqWaves;
         int ngroups = B * Hkv;
-        void *a[] = {&q, &k, &v, &idx, &lse, &dout, &dq, &delta, &Hq, &Hkv, &G, &T, &S,
+        void *a[] = {&q, &k, &v, &idx, &out, &lse, &dout, &dq, &delta, &Hq, &Hkv, &G, &T, &S,
                      &nq4, &ngroups, &score_scale, &scale};
         e = hipLaunchKernel((const void *)nsa_bwd_dq_kernel<D, BS>,
                             dim3((unsigned)(ngroups * nq4)), dim3(64 * kDqWaves), a, 0, stream);
@@ -696,15 +689,15 @@ size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int block_size, int 
 }
 
 hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                              const int32_t *block_idx, const float *lse, const uint16_t *dout,
-                              uint16_t *dq, uint16_t *dk, uint16_t *dv, void *workspace, int B,
-                              int Hq, int Hkv, int T, int D, int block_size, int S,
-                              hipStream_t stream) {
+                              const int32_t *block_idx, const uint16_t *out, const float *lse,
+                              const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                              void *workspace, int B, int Hq, int Hkv, int T, int D,
+                              int block_size, int S, hipStream_t stream) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
 #define ATTN_NSA_BWD_CASE(DD, BB)                                                            \
     if (D == DD && block_size == BB)                                                        \
-        return launch<DD, BB>(q, k, v, block_idx, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, \
-                              stream);
+        return launch<DD, BB>(q, k, v, block_idx, out, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, \
+                              S, stream);
     ATTN_NSA_BWD_CASE(128, 64)
     ATTN_NSA_BWD_CASE(128, 32)
     ATTN_NSA_BWD_CASE(128, 128)

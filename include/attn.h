@@ -192,16 +192,16 @@ int nsa_sel_fwd(const void *q, const void *k, const void *v, const int32_t *bloc
  *
  * With A_i the attended set of query i (as in the forward), s_ij = (q_i . k_j)
  * / sqrt(D), P_ij = exp(s_ij - lse_i), dP_ij = dout_i . v_j, delta_i =
- * sum_{j in A_i} P_ij dP_ij and dS_ij = P_ij (dP_ij - delta_i), for each head h
- * of kv group kv:
+ * sum_{j in A_i} P_ij dP_ij (= dout_i . out_i) and dS_ij = P_ij (dP_ij - delta_i),
+ * for each head h of kv group kv:
  *   dq_i = sum_{j in A_i} dS_ij k_j / sqrt(D)
  *   dk_j = sum_{h in group, i : j in A_i} dS_ij q_i / sqrt(D)
  *   dv_j = sum_{h in group, i : j in A_i} P_ij dout_i
  *
- *   q, dout      : bf16 [B, Hq, T, D]
+ *   q, dout, out : bf16 [B, Hq, T, D]   (out and lse as returned by nsa_sel_fwd)
  *   k, v         : bf16 [B, Hkv, T, D]
  *   block_idx    : int32 [B, Hkv, T, S]
- *   lse          : fp32 [B, Hq, T]      (as returned by nsa_sel_fwd)
+ *   lse          : fp32 [B, Hq, T]
  *   dq           : bf16 [B, Hq, T, D]   (written)
  *   dk, dv       : bf16 [B, Hkv, T, D]  (written; a key row no query attends gets 0)
  *   workspace    : device memory the call overwrites, at least
@@ -211,13 +211,15 @@ int nsa_sel_fwd(const void *q, const void *k, const void *v, const int32_t *bloc
  *   sizes        : as nsa_sel_fwd; in addition Hq*T*D*2 < 2^31 (else
  *                  ATTN_ERR_UNSUPPORTED).
  *
- * Numerics: scores, dP and delta in fp32 from bf16 products (delta from the
- * recomputed probabilities, not from the forward's rounded output); P and dS
- * rounded to bf16 before the products that consume them; fp32 accumulation;
- * every gradient row has one writer (no atomics on values): deterministic.
+ * Numerics: scores, dP and delta in fp32 from bf16 products.  delta is summed
+ * from the recomputed probabilities; dout . out (out is bf16) serves only as an
+ * estimate m of it, with dq = scale (sum_j P_ij (dP_ij - m) k_j - (delta_i - m)
+ * sum_j P_ij k_j).  P and dS rounded to bf16 before the products that consume
+ * them; fp32 accumulation; every gradient row has one writer (no atomics on
+ * values): deterministic.
  */
 int nsa_sel_bwd(const void *q, const void *k, const void *v, const int32_t *block_idx,
-                const float *lse, const void *dout,
+                const void *out, const float *lse, const void *dout,
                 void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
                 int B, int Hq, int Hkv, int T, int D, int block_size, int S, void *stream);
 

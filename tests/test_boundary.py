@@ -137,15 +137,16 @@ def test_tda_validation(lib):
     assert _tda(lib, q1=None, q2=None, k1=None, k2=None, v=None, o=None, ws=None, T=0) == OK
 
 
-def _nbwd(lib, q=P, k=P, v=P, idx=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 40,
+def _nbwd(lib, q=P, k=P, v=P, idx=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, ws=P, wsb=1 << 40,
           B=1, Hq=8, Hkv=2, T=128, D=128, bs=64, S=4):
-    return lib.nsa_sel_bwd(q, k, v, idx, lse, do, dq, dk, dv, ws, wsb, B, Hq, Hkv, T, D, bs,
+    return lib.nsa_sel_bwd(q, k, v, idx, o, lse, do, dq, dk, dv, ws, wsb, B, Hq, Hkv, T, D, bs,
                            S, None)
 
 
 def test_nsa_bwd_validation(lib):
     assert lib.nsa_sel_bwd_workspace_bytes(1, 8, 2, 128, 128, 64, 4) > 0
     assert lib.nsa_sel_bwd_workspace_bytes(1, 8, 2, 100, 128, 64, 4) == 0   # T % bs
+    assert _nbwd(lib, o=None) == ENULL
     assert _nbwd(lib, lse=None) == ENULL
     assert _nbwd(lib, do=None) == ENULL
     assert _nbwd(lib, dk=None) == ENULL
@@ -157,7 +158,7 @@ def test_nsa_bwd_validation(lib):
     assert _nbwd(lib, wsb=16) == EWORK
     assert _nbwd(lib, ws=P + 64) == EALIGN
     assert _nbwd(lib, dq=P + 8) == EALIGN
-    assert _nbwd(lib, B=0, q=None, k=None, v=None, idx=None, lse=None, do=None,
+    assert _nbwd(lib, B=0, q=None, k=None, v=None, idx=None, o=None, lse=None, do=None,
                  dq=None, dk=None, dv=None, ws=None) == OK
 
 

@@ -27,8 +27,8 @@ def _dout(shape, seed):
 
 def _run(q, k, v, idx, bs, do, dev):
     gq, gk, gv, gi, gdo = q.to(dev), k.to(dev), v.to(dev), torch.as_tensor(idx).to(dev), do.to(dev)
-    _, lse = cat.nsa_sel_fwd(gq, gk, gv, gi, bs)
-    g = cat.nsa_sel_bwd(gq, gk, gv, gi, bs, lse, gdo)
+    o, lse = cat.nsa_sel_fwd(gq, gk, gv, gi, bs)
+    g = cat.nsa_sel_bwd(gq, gk, gv, gi, bs, o, lse, gdo)
     torch.cuda.synchronize()
     return [x.cpu() for x in g]
 
