@@ -146,11 +146,10 @@ ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
 
 ATTN_EXPORT size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D,
                                                int block_size, int S) {
-    (void)D;
-    if (B <= 0 || Hq <= 0 || T <= 0 || block_size <= 0 || T % block_size != 0 || S < 1 ||
+    if (B <= 0 || Hq <= 0 || T <= 0 || D <= 0 || block_size <= 0 || T % block_size != 0 || S < 1 ||
         Hkv <= 0 || Hq % Hkv != 0)
         return 0;
-    return attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, block_size, S);
+    return attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, D, block_size, S);
 }
 
 ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
@@ -167,7 +166,7 @@ ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
     // per-batch byte offsets of q / dout rows must fit the 32-bit buffer addressing
     if ((int64_t)Hq * T * D * 2 >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
-    const size_t need = attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, block_size, S);
+    const size_t need = attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, D, block_size, S);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;
     const hipError_t e = attn::launch_nsa_sel_bwd(

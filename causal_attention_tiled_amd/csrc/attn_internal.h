@@ -70,7 +70,7 @@ hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16
                               void *workspace, int B, int Hq, int Hkv, int T, int D,
                               int block_size, int S, hipStream_t stream);
 // Workspace bytes of the NSA selection backward (block lists, per-row delta).
-size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int block_size, int S);
+size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
 hipError_t launch_tda_fwd_bf16(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,
                                const uint16_t *k2, const uint16_t *v, uint16_t *out,
                                uint16_t *workspace, int BH, int T, int D, float beta,

@@ -76,6 +76,46 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, void *lds, int voff, int soff)
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+
+// The same for 4 bytes per lane, to lds + 4 * lane.
+__device__ __forceinline__ void dma4(u32x4 rsrc, void *lds, int voff, int soff) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
+// Eight transposing LDS reads (ds_read_b64_tr_b16): r[2k] at LDS byte address
+// addr[k], r[2k+1] at addr[k] + OFF, in one statement that first waits until at most
+// VM of this wave's memory instructions are outstanding (s_waitcnt vmcnt(VM)) and
+// ends with lgkmcnt(0).  For a tile that arrived by LDS DMA this awaits exactly that
+// transfer (VM = the memory instructions issued after it), with nothing scheduled
+// between the wait and the reads, and the results are complete when the statement
+// ends.  The compiler sees no LDS read here, so it adds no wait of its own for the
+// DMA (which would be vmcnt(0): it cannot tell the tiles apart, and that would also
+// drain the loads of the next chunk).
+template <int VM, int OFF>
+__device__ __forceinline__ void tr_read4x2(bf16x4_t (&r)[8], const uint32_t (&addr)[4]) {
+    static_assert(VM >= 0 && VM < 64 && OFF >= 0 && OFF < 65536, "immediates");
+    asm volatile(
+        "s_waitcnt vmcnt(%12)\n\t"
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(VM), "n"(OFF)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
 #pragma clang diagnostic pop
 
 

@@ -36,6 +36,9 @@
 //    memory unit, with lse, delta and position in a small table.  S = Q K^T and
 //    dP = dO V^T (one key per lane), then dV^T += dO^T P and dK^T += Q^T dS with dO^T
 //    and Q^T read transposed from LDS.  Each key row has one writer: deterministic.
+#include <algorithm>
+#include <type_traits>
+
 #include "attn_tile.h"
 
 namespace attn {
@@ -44,6 +47,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;  // keys per processed chunk in the dq kernel
 constexpr int kDqWaves = 4;
+constexpr int kSegQ = 512;  // most queries of one (group, block) list per dk/dv workgroup
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -60,7 +64,7 @@ __device__ __forceinline__ void bwd_dma16(__amdgpu_buffer_rsrc_t r, void *lds, i
 // LDS K chunk (32 rows x D*2 bytes) swizzle for the transposing reads (as the
 // forward's V tile): chunk c of row r at slot c ^ swz(r).
 template <int D>
-__device__ __forceinline__ int chunk_swz(int row) {
+__host__ __device__ constexpr int chunk_swz(int row) {
     if constexpr (D == 128)
         return (row & 7) << 1;
     else
@@ -244,16 +248,16 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
         kdma_off[j] = row * ROWB + ((slot ^ chunk_swz<D>(row)) << 4);
     }
-    // K^T operand reads: rows 4*g4 + s/4 (+16), dims 16*dt + 4*(s%4)
-    int krd_off[NDT][2];
+    // K^T operand reads: rows 4*g4 + s/4 (and 16 rows further, same swizzle), dims
+    // 16*dt + 4*(s%4)
+    static_assert(chunk_swz<D>(16) == chunk_swz<D>(0), "upper keys: same swizzle");
+    int krd_off[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 4 * g4 + (n16 >> 2) + 16 * h;
-            const int col = 16 * dt + 4 * (n16 & 3);
-            krd_off[dt][h] = row * ROWB + (((col >> 3) ^ chunk_swz<D>(row)) << 4) + (col & 7) * 2;
-        }
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int row = 4 * g4 + (n16 >> 2);
+        const int col = 16 * dt + 4 * (n16 & 3);
+        krd_off[dt] = row * ROWB + (((col >> 3) ^ chunk_swz<D>(row)) << 4) + (col & 7) * 2;
+    }
 
     typedef uint8_t KTileBuf[kDqWaves][KTILE];
     bf16x8 kfa[2][NDS], vfa[2][NDS], kfb[2][NDS], vfb[2][NDS];
@@ -309,8 +313,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     }
 
     float dl = 0.0f;  // this lane's part of delta
+    // VM: memory instructions issued after this chunk's K transfer (the next chunk's, or
+    // none): the K^T reads wait for exactly this chunk's DMA.
+    constexpr int NEXT_OPS = 4 * NDS + KDMA;
     auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const bf16x8 (&vf)[2][NDS],
-                             const KTileBuf &kt) {
+                             const KTileBuf &kt, auto vm) {
+        constexpr int VM = decltype(vm)::value;
         f32x4 pr[2], dp[2];
         scores(k0, kf, vf, pr, dp);
         bf16x8 xf, yf;
@@ -323,18 +331,28 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
                 yf[kk * 4 + j] = (__bf16)pr[kk][j];
             }
         // X^T += K^T xf^T, Y^T += K^T yf^T
+        const uint32_t base = lds_addr(&kt[wave][0]);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint8_t *base = &kt[wave][0];
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(base + krd_off[dt][0]));
-            const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(base + krd_off[dt][1]));
-            const bf16x8 kt8 = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-            xacc[dt] = mfma_16x16x32(kt8, xf, xacc[dt]);
-            yacc[dt] = mfma_16x16x32(kt8, yf, yacc[dt]);
+        for (int d4 = 0; d4 < NDT; d4 += 4) {
+            uint32_t ad[4];
+            bf16x4_t rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + krd_off[d4 + e];
+            if (d4 == 0)
+                tr_read4x2<VM, 16 * ROWB>(rd, ad);
+            else
+                tr_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x8 kt8 = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3,
+                                                           4, 5, 6, 7);
+                xacc[d4 + e] = mfma_16x16x32(kt8, xf, xacc[d4 + e]);
+                yacc[d4 + e] = mfma_16x16x32(kt8, yf, yacc[d4 + e]);
+            }
         }
     };
+    using next_loaded = std::integral_constant<int, NEXT_OPS>;
+    using none_loaded = std::integral_constant<int, 0>;
 
     int cur_blk = -1, cur_c = 0;
     auto next_chunk = [&]() -> int {
@@ -350,21 +368,28 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         return cur_blk * BS;
     };
 
+    // chunks alternate between (kfa, vfa, kbuf_a) and (kfb, vfb, kbuf_b), each fetched
+    // one chunk ahead; a chunk's K^T reads are complete when compute_chunk returns, so
+    // its tile may be refilled right after
     int ka = next_chunk();
     if (ka >= 0) load_chunk(ka, kfa, vfa, kbuf_a);
     int kb = ka >= 0 ? next_chunk() : -1;
     while (ka >= 0) {
-        if (kb >= 0) load_chunk(kb, kfb, vfb, kbuf_b);
-        compute_chunk(ka, kfa, vfa, kbuf_a);
-        if (kb < 0) break;
+        if (kb >= 0) {
+            load_chunk(kb, kfb, vfb, kbuf_b);
+            compute_chunk(ka, kfa, vfa, kbuf_a, next_loaded{});
+        } else {
+            compute_chunk(ka, kfa, vfa, kbuf_a, none_loaded{});
+            break;
+        }
         ka = next_chunk();
         if (ka >= 0) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of kbuf_a done
             load_chunk(ka, kfa, vfa, kbuf_a);
+            compute_chunk(kb, kfb, vfb, kbuf_b, next_loaded{});
+        } else {
+            compute_chunk(kb, kfb, vfb, kbuf_b, none_loaded{});
         }
-        compute_chunk(kb, kfb, vfb, kbuf_b);
         kb = ka >= 0 ? next_chunk() : -1;
-        if (kb >= 0) __builtin_amdgcn_s_waitcnt(0xC07F);
     }
 
     dl += __shfl_xor(dl, 16);
@@ -388,44 +413,78 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
 // dk / dv (block-outer over the inverted CSR)
 // ---------------------------------------------------------------------------
 
+// one thread per (group, block) list: its segments of at most kSegQ queries (at least
+// one, so that a block nothing attends still has its zero gradients written) and the
+// partial results they leave (none when there is one segment)
+__global__ __launch_bounds__(256) void seg_count_kernel(const int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ nseg,
+                                                        int32_t *__restrict__ npart,
+                                                        int64_t nlists) {
+    const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (l >= nlists) return;
+    const int nq = offsets[l + 1] - offsets[l];
+    const int s = nq > kSegQ ? (nq + kSegQ - 1) / kSegQ : 1;
+    nseg[l] = s;
+    npart[l] = s > 1 ? s : 0;
+}
+
+// one thread per list: seg_list[k] = list of segment k
+__global__ __launch_bounds__(256) void seg_fill_kernel(const int32_t *__restrict__ seg_start,
+                                                       int32_t *__restrict__ seg_list,
+                                                       int64_t nlists) {
+    const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (l >= nlists) return;
+    for (int k = seg_start[l]; k < seg_start[l + 1]; ++k) seg_list[k] = (int)l;
+}
+
+// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const float *__restrict__ LSE,
     const uint16_t *__restrict__ dO, const float *__restrict__ DELTA,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ list,
-    uint16_t *__restrict__ dK, uint16_t *__restrict__ dV, int Hq, int Hkv, int G, int T,
-    int nblk, float score_scale, float scale) {
+    const int32_t *__restrict__ seg_start, const int32_t *__restrict__ seg_list,
+    const int32_t *__restrict__ part_start, float *__restrict__ part, uint16_t *__restrict__ dK,
+    uint16_t *__restrict__ dV, int Hq, int Hkv, int G, int T, int nblk, int nlists,
+    float score_scale, float scale) {
     constexpr int NW = BS / 32;                  // one wave per 32 keys of the block
+    constexpr int NBUF = BS == 32 ? 2 : 4;       // staged chunks (ring)
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
     constexpr int TILEB = 32 * ROWB;             // 32 gathered rows of one tensor
     constexpr int LOADS = 32 * CH / (64 * NW);   // 16-byte chunks per lane per tensor
+    constexpr int OPS = 2 * LOADS + 2;           // memory instructions per wave per chunk
     constexpr int NDS = D / 16;
     constexpr int NDT = D / 32;
-    constexpr int QB = 0, OB = 2 * TILEB;        // Q rows (2 buffers), then dO rows
     static_assert(LOADS >= 1 && 32 * CH % (64 * NW) == 0, "row staging");
+    static_assert((NBUF - 2) * OPS < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * TILEB];
-    // per staged row: lse' (base 2), delta, query position (-1: no row)
-    __shared__ __attribute__((aligned(16))) float rlse[2][32];
-    __shared__ __attribute__((aligned(16))) float rdelta[2][32];
-    __shared__ __attribute__((aligned(16))) int rpos[2][32];
+    // buffer u: Q rows at tile 2u, dO rows at tile 2u+1
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NBUF * 2 * TILEB];
+    // per staged row: lse (natural), delta, query position (-1: no row)
+    __shared__ __attribute__((aligned(16))) float rlse[NBUF][32];
+    __shared__ __attribute__((aligned(16))) float rdelta[NBUF][32];
+    __shared__ __attribute__((aligned(16))) int rpos[NBUF][32];
+    __shared__ int qpos[kSegQ];
 
-    // workgroup -> (group, block); blocks with the most attending queries (small ids)
-    // first, groups spread over the XCDs
-    const int ngroups = gridDim.x / nblk;
-    int group, blk;
-    if ((ngroups & 7) == 0) {
-        const int bid = blockIdx.x, xcd = bid & 7, s = bid >> 3, gpx = ngroups >> 3;
-        group = xcd * gpx + s % gpx;
-        blk = s / gpx;
-    } else {
-        group = blockIdx.x % ngroups;
-        blk = blockIdx.x / ngroups;
-    }
-    group = __builtin_amdgcn_readfirstlane(group);
-    blk = __builtin_amdgcn_readfirstlane(blk);
+    // workgroup -> segment: each XCD takes a contiguous range of segments (lists in
+    // (group, block) order, so the heavily attended early blocks come first)
+    const int seg_total = seg_start[nlists];
+    const int per = (seg_total + 7) >> 3;
+    const int wgi = blockIdx.x >> 3;
+    const int sidx = (blockIdx.x & 7) * per + wgi;
+    if (wgi >= per || sidx >= seg_total) return;  // whole workgroup: before any barrier
+    const int l = __builtin_amdgcn_readfirstlane(seg_list[sidx]);
+    const int seg = sidx - seg_start[l];
+    const bool multi = seg_start[l + 1] - seg_start[l] > 1;
+    const int group = l / nblk, blk = l % nblk;
     const int b = group / Hkv, kv = group % Hkv;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,18 +493,37 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     const int kw0 = blk * BS + 32 * wave;        // this wave's keys
     const int mykey = kw0 + l32;
 
-    const int lbeg = offsets[group * nblk + blk];
-    const int nq = offsets[group * nblk + blk + 1] - lbeg;
-    const int32_t *qlist = list + lbeg;
+    const int lbeg = offsets[l] + seg * kSegQ;
+    const int nq = min(kSegQ, offsets[l + 1] - lbeg);
     const int qc = 32 / G;                       // queries per chunk of rows
     const int rows_used = qc * G;
     const int nchunks = (nq + qc - 1) / qc;
 
-    // Q and dO of batch b: rows (h, i) at ((h*T + i) * ROWB)
-    const size_t bslab = (size_t)b * Hq * T * D;
+    // K and V rows of this wave's keys as B operands (before any DMA: in-order waits)
+    bf16x8 kf[NDS], vf[NDS];
+    {
+        const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) {
+            u32x4 a = zero4, c = zero4;
+            if (mykey < T) {
+                a = *(const u32x4 *)(K + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
+                c = *(const u32x4 *)(V + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
+            }
+            kf[ds] = as_bf16x8(a);
+            vf[ds] = as_bf16x8(c);
+        }
+    }
+    for (int t = tid; t < nq; t += 64 * NW) qpos[t] = list[lbeg + t];
+
+    // Q, dO, lse and delta of batch b: row (h, i) at (h*T + i)
+    const size_t bslab = (size_t)b * Hq * T;
     const uint32_t bbytes = (uint32_t)((size_t)Hq * T * ROWB);
-    const __amdgpu_buffer_rsrc_t rq = bwd_rsrc(Q + bslab, bbytes);
-    const __amdgpu_buffer_rsrc_t ro = bwd_rsrc(dO + bslab, bbytes);
+    const uint32_t tbytes = (uint32_t)((size_t)Hq * T * 4);
+    const u32x4 rq = make_rsrc(Q + bslab * D, bbytes);
+    const u32x4 ro = make_rsrc(dO + bslab * D, bbytes);
+    const u32x4 rl = make_rsrc(LSE + bslab, tbytes);
+    const u32x4 rd = make_rsrc(DELTA + bslab, tbytes);
 
     // staging positions: DMA instruction j of wave w fills tile bytes
     // [(w*LOADS + j)*1024, +1024); lane l the 16 bytes at +16*l, i.e. row r = pos / ROWB
@@ -457,35 +535,30 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
         srow[j] = pos / ROWB;
         sslot[j] = ((pos % ROWB) >> 4) ^ tile_swz<D>(pos / ROWB);
     }
-    auto stage = [&](int c, int buf) {
-        // row r of chunk c: query qlist[c*qc + r/G], head kv*G + r%G
+    // OPS memory instructions per wave: LOADS for Q, LOADS for dO, lse, delta.  Row r of
+    // chunk c is query qpos[c*qc + r/G], head kv*G + r%G; absent rows read as zero.
+    auto stage = [&](int c, int u) {
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             const int r = srow[j];
             const int qi = c * qc + r / G;
-            int off = (int)bbytes;  // past the end: reads zero
-            if (r < rows_used && qi < nq) {
-                const int h = kv * G + r % G;
-                off = (h * T + qlist[qi]) * ROWB + (sslot[j] << 4);
-            }
-            const int dst = buf * TILEB + (wave * LOADS + j) * 1024;
-            bwd_dma16(rq, &lds[QB + dst], off, 0);
-            bwd_dma16(ro, &lds[OB + dst], off, 0);
+            int off = (int)bbytes;
+            if (r < rows_used && qi < nq)
+                off = ((kv * G + r % G) * T + qpos[qi]) * ROWB + (sslot[j] << 4);
+            const int dst = (wave * LOADS + j) * 1024;
+            dma16(rq, &lds[(2 * u) * TILEB + dst], off, 0);
+            dma16(ro, &lds[(2 * u + 1) * TILEB + dst], off, 0);
         }
-        if (wave == 0 && lane < 32) {
+        if (lane < 32) {  // every wave writes the same table entries
             const int qi = c * qc + lane / G;
-            float ls = INFINITY, de = 0.0f;
-            int pos = -1;
+            int toff = (int)tbytes, pos = -1;
             if (lane < rows_used && qi < nq) {
-                const int h = kv * G + lane % G;
-                pos = qlist[qi];
-                const size_t rowid = (size_t)(b * Hq + h) * T + pos;
-                ls = LSE[rowid] * kLog2e;
-                de = DELTA[rowid];
+                pos = qpos[qi];
+                toff = ((kv * G + lane % G) * T + pos) * 4;
             }
-            rlse[buf][lane] = ls;
-            rdelta[buf][lane] = de;
-            rpos[buf][lane] = pos;
+            dma4(rl, &rlse[u][0], toff, 0);
+            dma4(rd, &rdelta[u][0], toff, 0);
+            rpos[u][lane] = pos;
         }
     };
 
@@ -504,11 +577,11 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
                           (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
                           8 * (s16 & 1);
         }
-    auto row_frag = [&](int base, int buf, int ds) {
-        return *(const bf16x8 *)(&lds[roff[ds] + base + buf * TILEB]);
+    auto row_frag = [&](int tile, int ds) {
+        return *(const bf16x8 *)(&lds[tile * TILEB + roff[ds]]);
     };
-    auto t_frag = [&](int base, int buf, int dt, int c) {
-        const uint8_t *p = &lds[base + buf * TILEB + 16 * c * ROWB];
+    auto t_frag = [&](int tile, int dt, int c) {
+        const uint8_t *p = &lds[tile * TILEB + 16 * c * ROWB];
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][0]));
         const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][1]));
         return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -519,49 +592,47 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkacc[dt][r] = dvacc[dt][r] = 0.0f;
-
-    if (nchunks > 0) stage(0, 0);
-    bf16x8 kf[NDS], vf[NDS];
-    {
-        const u32x4 zero4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            u32x4 a = zero4, c = zero4;
-            if (mykey < T) {
-                a = *(const u32x4 *)(K + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
-                c = *(const u32x4 *)(V + kvslab + (size_t)mykey * D + ds * 16 + hi * 8);
-            }
-            kf[ds] = as_bf16x8(a);
-            vf[ds] = as_bf16x8(c);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    __builtin_amdgcn_s_barrier();
-
     f32x16 zero16;
 #pragma unroll
     for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
 
+    // K and V rows and the query list are in: waited here once, so that no wait for
+    // them (which would also drain the staged chunks) lands inside the loop
+    wait_vm<0>();
+    __syncthreads();  // qpos
+    for (int c = 0; c < NBUF - 1 && c < nchunks; ++c) stage(c, c);
+
     for (int c = 0; c < nchunks; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < nchunks) stage(c + 1, buf ^ 1);
+        const int u = c % NBUF;
+        // chunk c's transfers are done once at most (chunks staged after it) * OPS remain
+        const int after = min(NBUF - 2, nchunks - 1 - c);
+        if constexpr (NBUF == 4) {
+            if (after >= 2) wait_vm<2 * OPS>();
+            else if (after == 1) wait_vm<OPS>();
+            else wait_vm<0>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();  // every wave's part of chunk c is in; chunk c-1 is consumed
+        if (c + NBUF - 1 < nchunks) stage(c + NBUF - 1, (c + NBUF - 1) % NBUF);
+
         // register r: row m = 8*(r/4) + 4*hi + r%4 of the chunk, key mykey (lane)
         f32x16 s = zero16, dp = zero16;
 #pragma unroll
         for (int ds = 0; ds < NDS; ++ds) {
-            s = mfma_32x32x16(row_frag(QB, buf, ds), kf[ds], s);
-            dp = mfma_32x32x16(row_frag(OB, buf, ds), vf[ds], dp);
+            s = mfma_32x32x16(row_frag(2 * u, ds), kf[ds], s);
+            dp = mfma_32x32x16(row_frag(2 * u + 1, ds), vf[ds], dp);
         }
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 ls = *(const f32x4 *)(&rlse[buf][8 * g + 4 * hi]);
-            const f32x4 de = *(const f32x4 *)(&rdelta[buf][8 * g + 4 * hi]);
-            const i32x4 ps = *(const i32x4 *)(&rpos[buf][8 * g + 4 * hi]);
+            const f32x4 ls = *(const f32x4 *)(&rlse[u][8 * g + 4 * hi]);
+            const f32x4 de = *(const f32x4 *)(&rdelta[u][8 * g + 4 * hi]);
+            const i32x4 ps = *(const i32x4 *)(&rpos[u][8 * g + 4 * hi]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * g + j;
-                float pr = __builtin_amdgcn_exp2f(s[r] * score_scale - ls[j]);
+                float pr = __builtin_amdgcn_exp2f(s[r] * score_scale - ls[j] * kLog2e);
                 if (mykey > ps[j]) pr = 0.0f;  // after the query (or no row: ps = -1)
                 pb[r >> 3][r & 7] = (__bf16)pr;
                 sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - de[j]));
@@ -571,14 +642,13 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                dvacc[dt] = mfma_32x32x16(t_frag(OB, buf, dt, cc), pb[cc], dvacc[dt]);
-                dkacc[dt] = mfma_32x32x16(t_frag(QB, buf, dt, cc), sb[cc], dkacc[dt]);
+                dvacc[dt] = mfma_32x32x16(t_frag(2 * u + 1, dt, cc), pb[cc], dvacc[dt]);
+                dkacc[dt] = mfma_32x32x16(t_frag(2 * u, dt, cc), sb[cc], dkacc[dt]);
             }
-        __builtin_amdgcn_s_waitcnt(0x0070);
-        __builtin_amdgcn_s_barrier();
     }
 
-    if (mykey < T) {
+    if (mykey >= T) return;
+    if (!multi) {
         uint16_t *krow = dK + kvslab + (size_t)mykey * D;
         uint16_t *vrow = dV + kvslab + (size_t)mykey * D;
 #pragma unroll
@@ -592,25 +662,79 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
                 *(u32x2 *)(krow + dt * 32 + 8 * i4 + 4 * hi) = kp;
                 *(u32x2 *)(vrow + dt * 32 + 8 * i4 + 4 * hi) = vp;
             }
+    } else {
+        // fp32 partial of this segment: [2][BS][D], dK unscaled
+        float *pk = part + (size_t)(part_start[l] + seg) * 2 * BS * D + (size_t)(32 * wave + l32) * D;
+        float *pv = pk + BS * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = dt * 32 + 8 * i4 + 4 * hi;
+                *(f32x4 *)(pk + d0) = f32x4{dkacc[dt][4 * i4], dkacc[dt][4 * i4 + 1],
+                                            dkacc[dt][4 * i4 + 2], dkacc[dt][4 * i4 + 3]};
+                *(f32x4 *)(pv + d0) = f32x4{dvacc[dt][4 * i4], dvacc[dt][4 * i4 + 1],
+                                            dvacc[dt][4 * i4 + 2], dvacc[dt][4 * i4 + 3]};
+            }
     }
 }
 
-// Workspace layout (all 256-byte aligned): bitmap, counts, offsets, list, delta.
+// Lists split over several segments: dK = scale * (sum of the partials), dV = sum, in
+// segment order.  (BS*D/1024) workgroups per list, 4 consecutive values per thread.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(
+    const float *__restrict__ part, const int32_t *__restrict__ seg_start,
+    const int32_t *__restrict__ part_start, uint16_t *__restrict__ dK, uint16_t *__restrict__ dV,
+    int T, int nblk, float scale) {
+    constexpr int WPL = BS * D / 1024;
+    const int l = blockIdx.x / WPL;
+    const int ns = seg_start[l + 1] - seg_start[l];
+    if (ns <= 1) return;
+    const int e = ((blockIdx.x % WPL) * 256 + threadIdx.x) * 4;  // < BS*D
+    const float *p = part + (size_t)part_start[l] * 2 * BS * D + e;
+    f32x4 sk = {0.0f, 0.0f, 0.0f, 0.0f}, sv = sk;
+    for (int s = 0; s < ns; ++s) {
+        sk += *(const f32x4 *)(p + (size_t)s * 2 * BS * D);
+        sv += *(const f32x4 *)(p + (size_t)s * 2 * BS * D + BS * D);
+    }
+    const int group = l / nblk, blk = l % nblk;
+    const size_t o = ((size_t)group * T + blk * BS) * D + e;
+    *(u32x2 *)(dK + o) = u32x2{pack_bf16x2(scale * sk[0], scale * sk[1]),
+                               pack_bf16x2(scale * sk[2], scale * sk[3])};
+    *(u32x2 *)(dV + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+}
+
+// Workspace layout (all 256-byte aligned): bitmap, counts, offsets, list, delta, nseg,
+// npart, seg_start, part_start, seg_list, partials.  Bounds, with P = B*Hkv*T*min(S, nblk)
+// the most (group, query, block) triples a selection can hold: segments <= nlists +
+// P/kSegQ; partial segments (lists longer than kSegQ) < 2P/kSegQ.
 struct BwdLayout {
-    size_t bits, counts, offsets, list, delta, total;
+    size_t bits, counts, offsets, list, delta, nseg, npart, seg_start, part_start, seg_list,
+        part, total;
+    int64_t max_segs;
 };
 
-BwdLayout layout(int B, int Hq, int Hkv, int T, int bs, int S) {
+BwdLayout layout(int B, int Hq, int Hkv, int T, int D, int bs, int S) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t nlists = (size_t)B * Hkv * (T / bs);
+    const int nblk = T / bs;
+    const size_t nlists = (size_t)B * Hkv * nblk;
     const size_t words = ((size_t)T + 31) / 32;
+    const size_t pairs = (size_t)B * Hkv * T * (size_t)std::min(S, nblk);
     BwdLayout L;
+    L.max_segs = (int64_t)(nlists + pairs / kSegQ);
+    const size_t max_part = 2 * pairs / kSegQ + 1;
     L.bits = 0;
     L.counts = al(L.bits + nlists * words * 4);
     L.offsets = al(L.counts + nlists * 4);
     L.list = al(L.offsets + (nlists + 1) * 4);
-    L.delta = al(L.list + (size_t)B * Hkv * T * S * 4);
-    L.total = al(L.delta + (size_t)B * Hq * T * 4);
+    L.delta = al(L.list + pairs * 4);
+    L.nseg = al(L.delta + (size_t)B * Hq * T * 4);
+    L.npart = al(L.nseg + nlists * 4);
+    L.seg_start = al(L.npart + nlists * 4);
+    L.part_start = al(L.seg_start + (nlists + 1) * 4);
+    L.seg_list = al(L.part_start + (nlists + 1) * 4);
+    L.part = al(L.seg_list + (size_t)L.max_segs * 4);
+    L.total = al(L.part + max_part * 2 * bs * D * 4);
     return L;
 }
 
@@ -619,18 +743,26 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
                   uint16_t *dk, uint16_t *dv, uint8_t *ws, int B, int Hq, int Hkv, int T, int S,
                   hipStream_t stream) {
-    const BwdLayout L = layout(B, Hq, Hkv, T, BS, S);
+    const BwdLayout L = layout(B, Hq, Hkv, T, D, BS, S);
     uint32_t *bits = (uint32_t *)(ws + L.bits);
     int32_t *counts = (int32_t *)(ws + L.counts);
     int32_t *offsets = (int32_t *)(ws + L.offsets);
     int32_t *list = (int32_t *)(ws + L.list);
     float *delta = (float *)(ws + L.delta);
+    int32_t *nseg = (int32_t *)(ws + L.nseg);
+    int32_t *npart = (int32_t *)(ws + L.npart);
+    int32_t *seg_start = (int32_t *)(ws + L.seg_start);
+    int32_t *part_start = (int32_t *)(ws + L.part_start);
+    int32_t *seg_list = (int32_t *)(ws + L.seg_list);
+    float *part = (float *)(ws + L.part);
     int nblk = T / BS;
     int words = (T + 31) / 32;
     int64_t nlists = (int64_t)B * Hkv * nblk;
+    int nl = (int)nlists;
     int G = Hq / Hkv;
     float score_scale = kLog2e / sqrtf((float)D);
     float scale = 1.0f / sqrtf((float)D);
+    const unsigned lgrid = (unsigned)((nlists + 255) / 256);
     hipError_t e;
     {
         int64_t n = nlists * words;
@@ -654,8 +786,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
         if (e != hipSuccess) return e;
     }
     {
-        int n = (int)nlists;
-        void *a[] = {&counts, &offsets, &n};
+        void *a[] = {&counts, &offsets, &nl};
         e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
         if (e != hipSuccess) return e;
     }
@@ -663,6 +794,26 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
         void *a[] = {&bits, &offsets, &list, &words, &nlists};
         e = hipLaunchKernel((const void *)csr_fill_kernel, dim3((unsigned)((nlists + 3) / 4)),
                             dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&offsets, &nseg, &npart, &nlists};
+        e = hipLaunchKernel((const void *)seg_count_kernel, dim3(lgrid), dim3(256), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&nseg, &seg_start, &nl};
+        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&npart, &part_start, &nl};
+        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&seg_start, &seg_list, &nlists};
+        e = hipLaunchKernel((const void *)seg_fill_kernel, dim3(lgrid), dim3(256), a, 0, stream);
         if (e != hipSuccess) return e;
     }
     {
@@ -675,17 +826,26 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
         if (e != hipSuccess) return e;
     }
     {
-        void *a[] = {&q, &k, &v, &lse, &dout, &delta, &offsets, &list, &dk, &dv, &Hq, &Hkv, &G,
-                     &T, &nblk, &score_scale, &scale};
-        return hipLaunchKernel((const void *)nsa_bwd_dkv_kernel<D, BS>,
-                               dim3((unsigned)nlists), dim3(64 * (BS / 32)), a, 0, stream);
+        const unsigned grid = (unsigned)(8 * ((L.max_segs + 7) / 8));
+        void *a[] = {&q, &k, &v, &lse, &dout, &delta, &offsets, &list, &seg_start, &seg_list,
+                     &part_start, &part, &dk, &dv, &Hq, &Hkv, &G, &T, &nblk, &nl,
+                     &score_scale, &scale};
+        e = hipLaunchKernel((const void *)nsa_bwd_dkv_kernel<D, BS>, dim3(grid),
+                            dim3(64 * (BS / 32)), a, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    {
+        void *a[] = {&part, &seg_start, &part_start, &dk, &dv, &T, &nblk, &scale};
+        return hipLaunchKernel((const void *)dkv_reduce_kernel<D, BS>,
+                               dim3((unsigned)(nlists * (BS * D / 1024))), dim3(256), a, 0,
+                               stream);
     }
 }
 
 }  // namespace
 
-size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int block_size, int S) {
-    return layout(B, Hq, Hkv, T, block_size, S).total;
+size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int D, int block_size, int S) {
+    return layout(B, Hq, Hkv, T, D, block_size, S).total;
 }
 
 hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -31,7 +31,9 @@
 //    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).
 //  * Workgroup order keeps each XCD on a contiguous range of (group, query) work so a
 //    group's K/V stays in one XCD's L2.
-#include "attn_internal.h"
+#include <type_traits>
+
+#include "attn_tile.h"
 
 namespace attn {
 namespace {
@@ -42,8 +44,6 @@ constexpr int kChunk = 32;  // keys per processed chunk
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 layout, range-checked).
@@ -58,16 +58,12 @@ __device__ __forceinline__ void nsa_dma16(__amdgpu_buffer_rsrc_t r, void *lds, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
-// Wait until this wave's LDS reads have returned (lgkmcnt(0); vmcnt and expcnt
-// untouched), so that an LDS tile it just read may be refilled.
-__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // V chunk in LDS: 32 rows (keys) x D*2 bytes, row-major; the 16-byte chunk c of row r
 // sits at chunk slot c ^ nsa_swz<D>(r).  A 16-lane group of the transposing read
 // takes 4 consecutive rows x 32 bytes; with this swizzle the 32 lanes served per
 // cycle (8 rows) cover all 64 banks once.
 template <int D>
-__device__ __forceinline__ int nsa_swz(int row) {
+__host__ __device__ constexpr int nsa_swz(int row) {
     if constexpr (D == 128)
         return (row & 7) << 1;          // one row per 256-byte bank line
     else
@@ -75,7 +71,7 @@ __device__ __forceinline__ int nsa_swz(int row) {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const int32_t *__restrict__ IDX, uint16_t *__restrict__ O,
     float *__restrict__ LSE, int Hq, int Hkv, int G, int T, int S, int nq4, int ngroups,
@@ -142,17 +138,17 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
         const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
         vdma_off[j] = row * ROWB + ((slot ^ nsa_swz<D>(row)) << 4);
     }
-    // V^T operand reads: rows 4*g4 + s/4 (+16 for the upper keys), dims 16*dt + 4*(s%4)
+    // V^T operand reads: rows 4*g4 + s/4 (and 16 rows further for the upper keys,
+    // same swizzle), dims 16*dt + 4*(s%4)
     const int s16 = n16;
-    int vrd_off[NDT][2];
+    static_assert(nsa_swz<D>(16) == nsa_swz<D>(0), "upper keys: same swizzle");
+    int vrd_off[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = 4 * g4 + (s16 >> 2) + 16 * h;
-            const int col = 16 * dt + 4 * (s16 & 3);  // element
-            vrd_off[dt][h] = row * ROWB + (((col >> 3) ^ nsa_swz<D>(row)) << 4) + (col & 7) * 2;
-        }
+    for (int dt = 0; dt < NDT; ++dt) {
+        const int row = 4 * g4 + (s16 >> 2);
+        const int col = 16 * dt + 4 * (s16 & 3);  // element
+        vrd_off[dt] = row * ROWB + (((col >> 3) ^ nsa_swz<D>(row)) << 4) + (col & 7) * 2;
+    }
 
     typedef uint8_t VTile[kWaves][VTILE];
     bf16x8 kfa[2][NDS], kfb[2][NDS];  // K operands of the two chunks in flight
@@ -175,7 +171,11 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const VTile &vt) {
+    // VM: memory instructions issued after this chunk's V transfer (those of the next
+    // chunk, or none): the V^T reads wait for exactly this chunk's DMA.
+    constexpr int NEXT_OPS = 2 * NDS + VDMA;
+    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const VTile &vt, auto vm) {
+        constexpr int VM = decltype(vm)::value;
         // S^T = K Q^T : register j of st[kk] is key k0 + 16*kk + 4*g4 + j, head n16
         f32x4 st[2];
 #pragma unroll
@@ -213,17 +213,27 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
             }
         lsum = lsum * alpha + psum;
         // O^T += V^T P^T : register j of oacc[dt] is dim 16*dt + 4*g4 + j, head n16
+        const uint32_t base = lds_addr(&vt[wave][0]);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint8_t *base = &vt[wave][0];
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(base + vrd_off[dt][0]));
-            const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4 *)(base + vrd_off[dt][1]));
-            const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-            oacc[dt] = mfma_16x16x32(a, pf, oacc[dt] * alpha);
+        for (int d4 = 0; d4 < NDT; d4 += 4) {
+            uint32_t ad[4];
+            bf16x4_t rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + vrd_off[d4 + e];
+            if (d4 == 0)
+                tr_read4x2<VM, 16 * ROWB>(rd, ad);
+            else
+                tr_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x8 a = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3, 4,
+                                                         5, 6, 7);
+                oacc[d4 + e] = mfma_16x16x32(a, pf, oacc[d4 + e] * alpha);
+            }
         }
     };
+    using next_loaded = std::integral_constant<int, NEXT_OPS>;
+    using none_loaded = std::integral_constant<int, 0>;
 
     // Walk the chunks of the kept blocks in slot order: chunk (blk, c) starts at key
     // blk*BS + 32*c and exists while it starts at or before i.
@@ -246,18 +256,24 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(
     int ka = next_chunk();
     if (ka >= 0) load_chunk(ka, kfa, vbuf_a);
     int kb = ka >= 0 ? next_chunk() : -1;
+    // (a chunk's V^T reads complete before compute_chunk returns, so its tile may be
+    // refilled right after)
     while (ka >= 0) {
-        if (kb >= 0) load_chunk(kb, kfb, vbuf_b);
-        compute_chunk(ka, kfa, vbuf_a);
-        if (kb < 0) break;
+        if (kb >= 0) {
+            load_chunk(kb, kfb, vbuf_b);
+            compute_chunk(ka, kfa, vbuf_a, next_loaded{});
+        } else {
+            compute_chunk(ka, kfa, vbuf_a, none_loaded{});
+            break;
+        }
         ka = next_chunk();
         if (ka >= 0) {
-            wait_lds_reads();  // this wave's reads of vbuf_a are done before it is refilled
             load_chunk(ka, kfa, vbuf_a);
+            compute_chunk(kb, kfb, vbuf_b, next_loaded{});
+        } else {
+            compute_chunk(kb, kfb, vbuf_b, none_loaded{});
         }
-        compute_chunk(kb, kfb, vbuf_b);
         kb = ka >= 0 ? next_chunk() : -1;
-        if (kb >= 0) wait_lds_reads();  // likewise for vbuf_b
     }
 
     // finalize: total sum of this head over its 4 lanes

@@ -33,8 +33,11 @@ def _run(q, k, v, idx, bs, do, dev):
     return [x.cpu() for x in g]
 
 
+# The last two select every causal block, so the early blocks are attended by more than
+# 512 queries and their dk/dv is summed from several workgroups' partial results.
 SMALL = [(1, 8, 2, 256, 128, 64, 4), (1, 4, 4, 128, 64, 32, 3), (2, 6, 2, 192, 128, 64, 5),
-         (1, 16, 1, 512, 128, 128, 8), (1, 8, 2, 256, 64, 64, 16), (1, 2, 1, 64, 128, 32, 2)]
+         (1, 16, 1, 512, 128, 128, 8), (1, 8, 2, 256, 64, 64, 16), (1, 2, 1, 64, 128, 32, 2),
+         (1, 4, 1, 1056, 64, 32, 33), (1, 8, 2, 1280, 128, 64, 20)]
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: "B%dHq%dHkv%dT%dD%dbs%dS%d" % c)
