@@ -46,9 +46,10 @@ CSRC = os.path.join(ROOT, "causal_attention_tiled_amd", "csrc")
 # sources whose change invalidates a recorded traffic figure of each kernel
 KERNEL_SOURCES = {
     "tra_fwd": ["tra_fwd.hip", "attn_internal.h", "attn_tile.h"],
-    "nsa_sel_fwd": ["nsa_sel_fwd.hip", "attn_internal.h"],
+    "nsa_sel_fwd": ["nsa_sel_fwd.hip", "attn_internal.h", "attn_tile.h"],
     "tda_fwd": ["tda_fwd.hip", "attn_internal.h", "attn_tile.h"],
     "tra_bwd": ["tra_bwd.hip", "attn_internal.h", "attn_tile.h"],
+    "nsa_sel_bwd": ["nsa_sel_bwd.hip", "nsa_index.hip", "attn_internal.h", "attn_tile.h"],
 }
 NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
 
@@ -192,11 +193,29 @@ def timed(fn, warm=10, per_launch=20, batch=50):
     return st
 
 
+def nsa_bwd(dev, q, k, v, gidx, bs, o, lse, gb, G, what, warm=5, per_launch=10, batch=10):
+    """Time nsa_sel_bwd on the forward's inputs; algorithmic bytes = the forward's gathered
+    K/V bytes plus 2*G*D*2 bytes of q and dout per (group, query, block) visit."""
+    do = torch.randn(*q.shape, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    S = gidx.shape[-1]
+    g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    ws = torch.empty(cat.nsa_sel_bwd_workspace_bytes(B, Hq, Hkv, T, D, bs, S), dtype=torch.uint8,
+                     device=dev)
+    st = timed(lambda: cat.nsa_sel_bwd(q, k, v, gidx, bs, o, lse, do, dq=g[0], dk=g[1], dv=g[2],
+                                       workspace=ws), warm, per_launch, batch)
+    total = gb * (1.0 + G / bs)
+    return {what: dict(st, algorithmic_gb=total / 1e9, gbps=total / (st["ms"] * 1e-3) / 1e9,
+                       workspace_gb=ws.numel() / 1e9)}
+
+
 def extra_configs(dev, nsa_c5=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
-    at T=4096; and NSA G=16 at T=32768 with L2 and MALL flushed before every launch."""
+    at T=4096 (forward and backward); and NSA G=16 at T=32768: backward, and forward
+    with L2 and MALL flushed before every launch."""
     res = {}
     B, H, T, D = 4, 16, 2048, 64
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
@@ -244,8 +263,13 @@ def extra_configs(dev, nsa_c5=None):
     st = timed(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), batch=50)
     res["nsa_sel_fwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"] = dict(
         st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
+    res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv,
+                       "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
+    del qn, kn, vn, gidx, o, lse
     if nsa_c5 is not None:
-        fn, gb = nsa_c5
+        fn, gb, t5 = nsa_c5
+        res.update(nsa_bwd(dev, *t5, gb, NSA["Hq"] // NSA["Hkv"],
+                           "nsa_sel_bwd B1 Hq64 Hkv4 T32768 D128 bs64 S16", 3, 5, 5))
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         st = stats(time_launches(fn, 2, 8, between=lambda: flush.fill_(1)))
         res["nsa_sel_fwd B1 Hq64 Hkv4 T32768 D128 bs64 S16, cold (512 MiB written before each launch)"] = dict(
@@ -385,7 +409,7 @@ def main():
     if not args.no_extra and args.only is None:
         print("bench: other configurations", file=sys.stderr, flush=True)
         c5 = (lambda: cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n),
-              gbytes)
+              gbytes, (gqn, gkn, gvn, gidx, NSA["block_size"], o_n, lse_n))
         result["other_configs"] = extra_configs(dev, nsa_c5=c5)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
