@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "tda_fwd": ["tda_fwd.hip", "attn_internal.h", "attn_tile.h"],
     "tra_bwd": ["tra_bwd.hip", "attn_internal.h", "attn_tile.h"],
     "nsa_sel_bwd": ["nsa_sel_bwd.hip", "nsa_index.hip", "attn_internal.h", "attn_tile.h"],
+    "nsa_sel_fwd_fsa": ["nsa_sel_fsa.hip", "nsa_index.hip", "attn_internal.h", "attn_tile.h"],
 }
 NSA = dict(B=1, Hq=64, Hkv=4, T=32768, D=128, block_size=64, S=16)
 
@@ -210,12 +211,29 @@ def nsa_bwd(dev, q, k, v, gidx, bs, o, lse, gb, G, what, warm=5, per_launch=10, 
                        workspace_gb=ws.numel() / 1e9)}
 
 
+def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, warm=5, per_launch=10, batch=20):
+    """Time the block-outer forward (same outputs as nsa_sel_fwd) on the same inputs;
+    the same algorithmic bytes as the query-outer kernel (the gathered K/V)."""
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    S = gidx.shape[-1]
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+    ws = torch.empty(cat.nsa_sel_fsa_workspace_bytes(B, Hq, Hkv, T, D, bs, S), dtype=torch.uint8,
+                     device=dev)
+    st = timed(lambda: cat.nsa_sel_fwd_fsa(q, k, v, gidx, bs, out=o, lse=lse, workspace=ws),
+               warm, per_launch, batch)
+    return {what: dict(st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9,
+                       workspace_gb=ws.numel() / 1e9)}
+
+
 def extra_configs(dev, nsa_c5=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
-    at T=4096 (forward and backward); and NSA G=16 at T=32768: backward, and forward
-    with L2 and MALL flushed before every launch."""
+    at T=4096 (forward, block-outer forward and backward); and NSA G=16 at T=32768:
+    block-outer forward, backward, and forward with L2 and MALL flushed before every
+    launch."""
     res = {}
     B, H, T, D = 4, 16, 2048, 64
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
@@ -263,11 +281,16 @@ def extra_configs(dev, nsa_c5=None):
     st = timed(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), batch=50)
     res["nsa_sel_fwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"] = dict(
         st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
+    res.update(nsa_fsa(dev, qn, kn, vn, gidx, bs, gb,
+                       "nsa_sel_fwd_fsa (block-outer) B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
     res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv,
                        "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
     del qn, kn, vn, gidx, o, lse
     if nsa_c5 is not None:
         fn, gb, t5 = nsa_c5
+        res.update(nsa_fsa(dev, *t5[:5], gb,
+                           "nsa_sel_fwd_fsa (block-outer) B1 Hq64 Hkv4 T32768 D128 bs64 S16",
+                           3, 5, 5))
         res.update(nsa_bwd(dev, *t5, gb, NSA["Hq"] // NSA["Hkv"],
                            "nsa_sel_bwd B1 Hq64 Hkv4 T32768 D128 bs64 S16", 3, 5, 5))
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -44,6 +44,10 @@ def load_library():
     lib.tra_fwd_f32.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, vp]
     lib.tra_fwd_f32.restype = ci
     lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 7 + [vp]
+    lib.nsa_sel_fwd_fsa.argtypes = [vp] * 7 + [ctypes.c_size_t] + [ci] * 7 + [vp]
+    lib.nsa_sel_fwd_fsa.restype = ci
+    lib.nsa_sel_fsa_workspace_bytes.argtypes = [ci] * 7
+    lib.nsa_sel_fsa_workspace_bytes.restype = ctypes.c_size_t
     lib.nsa_sel_bwd.restype = ci
     lib.nsa_sel_bwd_workspace_bytes.argtypes = [ci] * 7
     lib.nsa_sel_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -218,6 +222,57 @@ def nsa_sel_fwd(q, k, v, block_idx, block_size, out=None, lse=None, stream=None,
                                     _stream_handle(stream))
     if rc != 0:
         raise AttnError("nsa_sel_fwd", rc)
+    return out, lse
+
+
+def nsa_sel_fsa_workspace_bytes(B, Hq, Hkv, T, D, block_size, S) -> int:
+    """Bytes of device workspace nsa_sel_fwd_fsa needs."""
+    return int(load_library().nsa_sel_fsa_workspace_bytes(B, Hq, Hkv, T, D, block_size, S))
+
+
+def nsa_sel_fwd_fsa(q, k, v, block_idx, block_size, out=None, lse=None, workspace=None,
+                    stream=None, want_lse: bool = True):
+    """NSA selection-branch forward in block-outer form: the outputs of nsa_sel_fwd.
+
+    Arguments as nsa_sel_fwd; ``workspace`` (uint8 GPU tensor of at least
+    ``nsa_sel_fsa_workspace_bytes`` bytes) is allocated here when not given.
+    Returns (out, lse).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    _check(block_idx, "block_idx", torch.int32)
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, T, D]; k, v [B, Hkv, T, D]")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError("k, v must be [B, Hkv, T, D] matching q")
+    if block_idx.dim() != 4 or tuple(block_idx.shape[:3]) != (B, Hkv, T):
+        raise ValueError("block_idx must be [B, Hkv, T, S]")
+    S = block_idx.shape[3]
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", torch.bfloat16)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32)
+        if tuple(lse.shape) != (B, Hq, T):
+            raise ValueError("lse must be [B, Hq, T]")
+    need = nsa_sel_fsa_workspace_bytes(B, Hq, Hkv, T, D, int(block_size), S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(workspace, "workspace", torch.uint8)
+    rc = load_library().nsa_sel_fwd_fsa(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        block_idx.data_ptr(), out.data_ptr(),
+                                        lse.data_ptr() if lse is not None else None,
+                                        workspace.data_ptr(), workspace.numel(),
+                                        B, Hq, Hkv, T, D, int(block_size), S,
+                                        _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("nsa_sel_fwd_fsa", rc)
     return out, lse
 
 

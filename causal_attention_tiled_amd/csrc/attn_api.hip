@@ -178,6 +178,36 @@ ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+ATTN_EXPORT size_t nsa_sel_fsa_workspace_bytes(int B, int Hq, int Hkv, int T, int D,
+                                               int block_size, int S) {
+    if (B <= 0 || Hq <= 0 || T <= 0 || D <= 0 || block_size <= 0 || T % block_size != 0 || S < 1 ||
+        Hkv <= 0 || Hq % Hkv != 0)
+        return 0;
+    return attn::nsa_sel_fsa_workspace(B, Hq, Hkv, T, D, block_size, S);
+}
+
+ATTN_EXPORT int nsa_sel_fwd_fsa(const void *q, const void *k, const void *v,
+                                const int32_t *block_idx, void *out, float *lse, void *workspace,
+                                size_t workspace_bytes, int B, int Hq, int Hkv, int T, int D,
+                                int block_size, int S, void *stream) {
+    bool noop;
+    const int st = nsa_validate(q, k, v, block_idx, B, Hq, Hkv, T, D, block_size, S, &noop);
+    if (st != ATTN_OK || noop) return st;
+    if (!out) return ATTN_ERR_NULL;
+    if (misaligned(out)) return ATTN_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
+    // per-batch byte offsets of q rows must fit the 32-bit buffer addressing
+    if ((int64_t)Hq * T * D * 2 >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    const size_t need = attn::nsa_sel_fsa_workspace(B, Hq, Hkv, T, D, block_size, S);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;
+    const hipError_t e = attn::launch_nsa_sel_fsa(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), block_idx, static_cast<uint16_t *>(out), lse,
+        workspace, B, Hq, Hkv, T, D, block_size, S, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 ATTN_EXPORT const char *attn_status_str(int status) {
     switch (status) {
         case ATTN_OK: return "ok";

@@ -71,6 +71,28 @@ hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16
                               int block_size, int S, hipStream_t stream);
 // Workspace bytes of the NSA selection backward (block lists, per-row delta).
 size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
+
+// Inverted NSA selection (nsa_index.hip): per list (group * nblk + block) the
+// increasing positions of the queries attending the block, list offsets, per-word
+// ranks, and segments of at most kNsaSegQ queries.  pairs bounds the total list length,
+// max_segs the segments, max_part the segments of lists longer than kNsaSegQ.
+size_t nsa_sel_fsa_workspace(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
+hipError_t launch_nsa_sel_fsa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const int32_t *block_idx, uint16_t *out, float *lse,
+                              void *workspace, int B, int Hq, int Hkv, int T, int D,
+                              int block_size, int S, hipStream_t stream);
+
+constexpr int kNsaSegQ = 512;
+struct NsaIndex {
+    uint32_t *bits;
+    int32_t *rank, *counts, *offsets, *list, *nseg, *npart, *seg_start, *part_start, *seg_list;
+    int nblk, words;
+    int64_t nlists, pairs, max_segs, max_part;
+};
+// Pointers into ws (256-byte aligned, ws may be null to size only); *bytes = bytes used.
+NsaIndex nsa_index_carve(void *ws, int B, int Hkv, int T, int bs, int S, size_t *bytes);
+hipError_t nsa_index_build(const NsaIndex &ix, const int32_t *block_idx, int B, int Hkv, int T,
+                           int bs, int S, hipStream_t stream);
 hipError_t launch_tda_fwd_bf16(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,
                                const uint16_t *k2, const uint16_t *v, uint16_t *out,
                                uint16_t *workspace, int BH, int T, int D, float beta,

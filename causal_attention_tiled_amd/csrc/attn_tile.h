@@ -54,6 +54,13 @@ __device__ __forceinline__ int tile_swz(int row) {
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 
+// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Raw buffer resource (gfx9 layout) over `bytes` bytes at `base`, held in scalar
 // registers; loads past the end return 0.
 __device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {

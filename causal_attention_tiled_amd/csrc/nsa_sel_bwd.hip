@@ -12,12 +12,8 @@
 //     dk_j = scale sum_{h, i : j in A_i} dS_ij q_i,   dv_j = sum_{h, i : j in A_i} P_ij dout_i
 //
 // Kernels (all on the caller's stream, workspace from the caller):
-//  * CSR of the selection, inverted: for each (group, block) the increasing list of
-//    queries that attend it.  A bitmap per (group, block) over the query positions
-//    is set with atomic ORs (a repeated slot sets the same bit), its bits are
-//    counted per (group, block), one workgroup scans the counts, and one wave per
-//    (group, block) writes the positions of the set bits in order.  Every step's
-//    result is independent of scheduling.
+//  * The selection inverted (nsa_index.hip): for each (group, block) the increasing
+//    list of queries that attend it, cut into segments of at most kNsaSegQ queries.
 //  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
@@ -30,12 +26,14 @@
 //    correction term is small, so its bf16 operand costs nothing, and the rounding
 //    of the main term is the rounding of dS itself.  The kernel writes delta per
 //    (head, query) for the next kernel.
-//  * dk/dv: one workgroup per (group, block), one wavefront per 32 keys of the block
-//    holding its K and V rows in registers, the block's query list walked in chunks
-//    of 32 rows (query, head): their Q and dO rows are gathered into LDS by the
-//    memory unit, with lse, delta and position in a small table.  S = Q K^T and
-//    dP = dO V^T (one key per lane), then dV^T += dO^T P and dK^T += Q^T dS with dO^T
-//    and Q^T read transposed from LDS.  Each key row has one writer: deterministic.
+//  * dk/dv: one workgroup per segment of a (group, block) list, one wavefront per 32
+//    keys of the block holding its K and V rows in registers, the segment's queries
+//    walked in chunks of 32 rows (query, head): their Q and dO rows are gathered into
+//    LDS by the memory unit, four chunks ahead, with lse, delta and position in a
+//    small table.  S = Q K^T and dP = dO V^T (one key per lane), then dV^T += dO^T P
+//    and dK^T += Q^T dS with dO^T and Q^T read transposed from LDS.  A list of one
+//    segment writes its key rows; a longer list writes fp32 partials that a reduce
+//    kernel sums in segment order.  Each key row has one writer: deterministic.
 #include <algorithm>
 #include <type_traits>
 
@@ -47,7 +45,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;  // keys per processed chunk in the dq kernel
 constexpr int kDqWaves = 4;
-constexpr int kSegQ = 512;  // most queries of one (group, block) list per dk/dv workgroup
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -69,101 +66,6 @@ __host__ __device__ constexpr int chunk_swz(int row) {
         return (row & 7) << 1;
     else
         return ((row >> 1) & 3) << 1;
-}
-
-// ---------------------------------------------------------------------------
-// CSR build
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
-// one thread per (group, query, slot): set bit i of the (group, block) bitmap
-__global__ __launch_bounds__(256) void csr_bitmap_kernel(const int32_t *__restrict__ idx,
-                                                         uint32_t *__restrict__ bits, int T,
-                                                         int S, int nblk, int bs, int words,
-                                                         int64_t total) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
-    const int blk = idx[e];
-    const int64_t row = e / S;                // (group, i)
-    const int i = (int)(row % T);
-    const int64_t group = row / T;
-    if (blk < 0 || blk >= nblk || blk * bs > i) return;
-    atomicOr(&bits[(group * nblk + blk) * words + (i >> 5)], 1u << (i & 31));
-}
-
-// one wave per (group, block): number of attending queries
-__global__ __launch_bounds__(256) void csr_count_kernel(const uint32_t *__restrict__ bits,
-                                                        int32_t *__restrict__ counts, int words,
-                                                        int64_t nlists) {
-    const int64_t list = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (list >= nlists) return;
-    const uint32_t *w = bits + list * words;
-    int c = 0;
-    for (int k = lane; k < words; k += 64) c += __builtin_popcount(w[k]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
-    if (lane == 0) counts[list] = c;
-}
-
-// one workgroup: offsets[0] = 0, offsets[k+1] = offsets[k] + counts[k]
-__global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t *__restrict__ counts,
-                                                        int32_t *__restrict__ offsets,
-                                                        int nlists) {
-    __shared__ int32_t part[1024];
-    const int t = threadIdx.x;
-    const int per = (nlists + 1023) / 1024;
-    const int lo = min(t * per, nlists), hi = min(lo + per, nlists);
-    int s = 0;
-    for (int k = lo; k < hi; ++k) s += counts[k];
-    part[t] = s;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan of the per-thread sums
-        const int v = t >= d ? part[t - d] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
-    }
-    int run = t > 0 ? part[t - 1] : 0;
-    if (t == 0) offsets[0] = 0;
-    for (int k = lo; k < hi; ++k) {
-        run += counts[k];
-        offsets[k + 1] = run;
-    }
-}
-
-// one wave per (group, block): positions of the set bits, increasing
-__global__ __launch_bounds__(256) void csr_fill_kernel(const uint32_t *__restrict__ bits,
-                                                       const int32_t *__restrict__ offsets,
-                                                       int32_t *__restrict__ list, int words,
-                                                       int64_t nlists) {
-    const int64_t l = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (l >= nlists) return;
-    const uint32_t *w = bits + l * words;
-    int base = offsets[l];
-    for (int k0 = 0; k0 < words; k0 += 64) {
-        const int k = k0 + lane;
-        uint32_t x = k < words ? w[k] : 0u;
-        const int c = __builtin_popcount(x);
-        int incl = c;  // inclusive prefix over the wave
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const int y = __shfl_up(incl, m, 64);
-            if (lane >= m) incl += y;
-        }
-        int pos = base + incl - c;
-        while (x) {
-            const int bit = __builtin_ctz(x);
-            x &= x - 1;
-            list[pos++] = k * 32 + bit;
-        }
-        base += __shfl(incl, 63, 64);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -413,36 +315,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
 // dk / dv (block-outer over the inverted CSR)
 // ---------------------------------------------------------------------------
 
-// one thread per (group, block) list: its segments of at most kSegQ queries (at least
-// one, so that a block nothing attends still has its zero gradients written) and the
-// partial results they leave (none when there is one segment)
-__global__ __launch_bounds__(256) void seg_count_kernel(const int32_t *__restrict__ offsets,
-                                                        int32_t *__restrict__ nseg,
-                                                        int32_t *__restrict__ npart,
-                                                        int64_t nlists) {
-    const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (l >= nlists) return;
-    const int nq = offsets[l + 1] - offsets[l];
-    const int s = nq > kSegQ ? (nq + kSegQ - 1) / kSegQ : 1;
-    nseg[l] = s;
-    npart[l] = s > 1 ? s : 0;
-}
-
-// one thread per list: seg_list[k] = list of segment k
-__global__ __launch_bounds__(256) void seg_fill_kernel(const int32_t *__restrict__ seg_start,
-                                                       int32_t *__restrict__ seg_list,
-                                                       int64_t nlists) {
-    const int64_t l = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (l >= nlists) return;
-    for (int k = seg_start[l]; k < seg_start[l + 1]; ++k) seg_list[k] = (int)l;
-}
-
-// s_waitcnt with only vmcnt = n (expcnt and lgkmcnt at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
 
 template <int D, int BS>
 __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
@@ -472,7 +344,7 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     __shared__ __attribute__((aligned(16))) float rlse[NBUF][32];
     __shared__ __attribute__((aligned(16))) float rdelta[NBUF][32];
     __shared__ __attribute__((aligned(16))) int rpos[NBUF][32];
-    __shared__ int qpos[kSegQ];
+    __shared__ int qpos[kNsaSegQ];
 
     // workgroup -> segment: each XCD takes a contiguous range of segments (lists in
     // (group, block) order, so the heavily attended early blocks come first)
@@ -493,8 +365,8 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     const int kw0 = blk * BS + 32 * wave;        // this wave's keys
     const int mykey = kw0 + l32;
 
-    const int lbeg = offsets[l] + seg * kSegQ;
-    const int nq = min(kSegQ, offsets[l + 1] - lbeg);
+    const int lbeg = offsets[l] + seg * kNsaSegQ;
+    const int nq = min(kNsaSegQ, offsets[l + 1] - lbeg);
     const int qc = 32 / G;                       // queries per chunk of rows
     const int rows_used = qc * G;
     const int nchunks = (nq + qc - 1) / qc;
@@ -704,37 +576,27 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(
     *(u32x2 *)(dV + o) = u32x2{pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
 }
 
-// Workspace layout (all 256-byte aligned): bitmap, counts, offsets, list, delta, nseg,
-// npart, seg_start, part_start, seg_list, partials.  Bounds, with P = B*Hkv*T*min(S, nblk)
-// the most (group, query, block) triples a selection can hold: segments <= nlists +
-// P/kSegQ; partial segments (lists longer than kSegQ) < 2P/kSegQ.
+// Workspace: the inverted index, then delta [B*Hq*T] fp32, then the fp32 dk/dv partials
+// of split lists ([max_part][2][BS][D]).
 struct BwdLayout {
-    size_t bits, counts, offsets, list, delta, nseg, npart, seg_start, part_start, seg_list,
-        part, total;
-    int64_t max_segs;
+    NsaIndex ix;
+    float *delta, *part;
+    size_t total;
 };
 
-BwdLayout layout(int B, int Hq, int Hkv, int T, int D, int bs, int S) {
+BwdLayout layout(void *ws, int B, int Hq, int Hkv, int T, int D, int bs, int S) {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const int nblk = T / bs;
-    const size_t nlists = (size_t)B * Hkv * nblk;
-    const size_t words = ((size_t)T + 31) / 32;
-    const size_t pairs = (size_t)B * Hkv * T * (size_t)std::min(S, nblk);
     BwdLayout L;
-    L.max_segs = (int64_t)(nlists + pairs / kSegQ);
-    const size_t max_part = 2 * pairs / kSegQ + 1;
-    L.bits = 0;
-    L.counts = al(L.bits + nlists * words * 4);
-    L.offsets = al(L.counts + nlists * 4);
-    L.list = al(L.offsets + (nlists + 1) * 4);
-    L.delta = al(L.list + pairs * 4);
-    L.nseg = al(L.delta + (size_t)B * Hq * T * 4);
-    L.npart = al(L.nseg + nlists * 4);
-    L.seg_start = al(L.npart + nlists * 4);
-    L.part_start = al(L.seg_start + (nlists + 1) * 4);
-    L.seg_list = al(L.part_start + (nlists + 1) * 4);
-    L.part = al(L.seg_list + (size_t)L.max_segs * 4);
-    L.total = al(L.part + max_part * 2 * bs * D * 4);
+    size_t o;
+    L.ix = nsa_index_carve(ws, B, Hkv, T, bs, S, &o);
+    const size_t o_delta = o;
+    o = al(o + (size_t)B * Hq * T * 4);
+    const size_t o_part = o;
+    o = al(o + (size_t)L.ix.max_part * 2 * bs * D * 4);
+    L.total = o;
+    uint8_t *w = static_cast<uint8_t *>(ws);
+    L.delta = (float *)(w + o_delta);
+    L.part = (float *)(w + o_part);
     return L;
 }
 
@@ -743,79 +605,18 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                   const uint16_t *out, const float *lse, const uint16_t *dout, uint16_t *dq,
                   uint16_t *dk, uint16_t *dv, uint8_t *ws, int B, int Hq, int Hkv, int T, int S,
                   hipStream_t stream) {
-    const BwdLayout L = layout(B, Hq, Hkv, T, D, BS, S);
-    uint32_t *bits = (uint32_t *)(ws + L.bits);
-    int32_t *counts = (int32_t *)(ws + L.counts);
-    int32_t *offsets = (int32_t *)(ws + L.offsets);
-    int32_t *list = (int32_t *)(ws + L.list);
-    float *delta = (float *)(ws + L.delta);
-    int32_t *nseg = (int32_t *)(ws + L.nseg);
-    int32_t *npart = (int32_t *)(ws + L.npart);
-    int32_t *seg_start = (int32_t *)(ws + L.seg_start);
-    int32_t *part_start = (int32_t *)(ws + L.part_start);
-    int32_t *seg_list = (int32_t *)(ws + L.seg_list);
-    float *part = (float *)(ws + L.part);
+    const BwdLayout L = layout(ws, B, Hq, Hkv, T, D, BS, S);
+    const int32_t *offsets = L.ix.offsets, *list = L.ix.list, *seg_start = L.ix.seg_start;
+    const int32_t *seg_list = L.ix.seg_list, *part_start = L.ix.part_start;
+    float *delta = L.delta, *part = L.part;
     int nblk = T / BS;
-    int words = (T + 31) / 32;
-    int64_t nlists = (int64_t)B * Hkv * nblk;
+    int64_t nlists = L.ix.nlists;
     int nl = (int)nlists;
     int G = Hq / Hkv;
     float score_scale = kLog2e / sqrtf((float)D);
     float scale = 1.0f / sqrtf((float)D);
-    const unsigned lgrid = (unsigned)((nlists + 255) / 256);
-    hipError_t e;
-    {
-        int64_t n = nlists * words;
-        void *a[] = {&bits, &n};
-        e = hipLaunchKernel((const void *)fill_u32_kernel, dim3((unsigned)((n + 255) / 256)),
-                            dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        int64_t total = (int64_t)B * Hkv * T * S;
-        int bs = BS;
-        void *a[] = {&idx, &bits, &T, &S, &nblk, &bs, &words, &total};
-        e = hipLaunchKernel((const void *)csr_bitmap_kernel, dim3((unsigned)((total + 255) / 256)),
-                            dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&bits, &counts, &words, &nlists};
-        e = hipLaunchKernel((const void *)csr_count_kernel, dim3((unsigned)((nlists + 3) / 4)),
-                            dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&counts, &offsets, &nl};
-        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&bits, &offsets, &list, &words, &nlists};
-        e = hipLaunchKernel((const void *)csr_fill_kernel, dim3((unsigned)((nlists + 3) / 4)),
-                            dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&offsets, &nseg, &npart, &nlists};
-        e = hipLaunchKernel((const void *)seg_count_kernel, dim3(lgrid), dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&nseg, &seg_start, &nl};
-        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&npart, &part_start, &nl};
-        e = hipLaunchKernel((const void *)csr_scan_kernel, dim3(1), dim3(1024), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
-    {
-        void *a[] = {&seg_start, &seg_list, &nlists};
-        e = hipLaunchKernel((const void *)seg_fill_kernel, dim3(lgrid), dim3(256), a, 0, stream);
-        if (e != hipSuccess) return e;
-    }
+    hipError_t e = nsa_index_build(L.ix, idx, B, Hkv, T, BS, S, stream);
+    if (e != hipSuccess) return e;
     {
         int nq4 = (T + kDqWaves - 1) / kDqWaves;
         int ngroups = B * Hkv;
@@ -826,7 +627,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
         if (e != hipSuccess) return e;
     }
     {
-        const unsigned grid = (unsigned)(8 * ((L.max_segs + 7) / 8));
+        const unsigned grid = (unsigned)(8 * ((L.ix.max_segs + 7) / 8));
         void *a[] = {&q, &k, &v, &lse, &dout, &delta, &offsets, &list, &seg_start, &seg_list,
                      &part_start, &part, &dk, &dv, &Hq, &Hkv, &G, &T, &nblk, &nl,
                      &score_scale, &scale};
@@ -845,7 +646,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 }  // namespace
 
 size_t nsa_sel_bwd_workspace(int B, int Hq, int Hkv, int T, int D, int block_size, int S) {
-    return layout(B, Hq, Hkv, T, D, block_size, S).total;
+    return layout(nullptr, B, Hq, Hkv, T, D, block_size, S).total;
 }
 
 hipError_t launch_nsa_sel_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,

@@ -227,6 +227,36 @@ int nsa_sel_bwd(const void *q, const void *k, const void *v, const int32_t *bloc
  * the problem is empty). */
 size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
 
+/*
+ * NSA selection-branch forward in block-outer form: the same outputs as
+ * nsa_sel_fwd, computed block by block.
+ *
+ * Source: msb-msb/openbox-llm, page "nsa_selection_kernel.py" --
+ * `_selection_fwd_blockouter_kernel` (each selected key block loaded once, the
+ * queries that select it processed against it, a partial (max, sum, weighted
+ * sum) left per (query, block)) and `selection_forward_fsa` (the partials of a
+ * query merged with the log-sum-exp rule: one softmax over the union of its
+ * selected causal tokens).  Same arguments, semantics and limits as
+ * nsa_sel_fwd, plus:
+ *   workspace : device memory the call overwrites, at least
+ *               nsa_sel_fsa_workspace_bytes(...) bytes, 256-byte aligned (else
+ *               ATTN_ERR_WORKSPACE / ATTN_ERR_ALIGN); it holds the inverted
+ *               selection and one partial per (query, selected block, head).
+ *               Calls that share one workspace must not overlap in time.
+ *   sizes     : in addition Hq*T*D*2 < 2^31 (else ATTN_ERR_UNSUPPORTED).
+ *
+ * Numerics: scores fp32 from bf16 products; per block the row max, sum and
+ * weighted sum in fp32, probabilities rounded to bf16 before they multiply V,
+ * the block's normalised output stored in bf16; the merge in fp32; out bf16.
+ */
+int nsa_sel_fwd_fsa(const void *q, const void *k, const void *v, const int32_t *block_idx,
+                    void *out, float *lse, void *workspace, size_t workspace_bytes,
+                    int B, int Hq, int Hkv, int T, int D, int block_size, int S, void *stream);
+
+/* Workspace bytes nsa_sel_fwd_fsa needs for these sizes (0 if a size is invalid
+ * or the problem is empty). */
+size_t nsa_sel_fsa_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int block_size, int S);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char *attn_status_str(int status);
 

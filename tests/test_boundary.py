@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tra_fwd", "tra_fwd_f32", "tra_bwd", "tda_fwd", "tda_workspace_bytes",
-              "nsa_sel_fwd", "nsa_sel_bwd", "nsa_sel_bwd_workspace_bytes", "attn_status_str"):
+              "nsa_sel_fwd", "nsa_sel_bwd", "nsa_sel_bwd_workspace_bytes", "nsa_sel_fwd_fsa",
+              "nsa_sel_fsa_workspace_bytes", "attn_status_str"):
         assert n in names
 
 
@@ -160,6 +161,32 @@ def test_nsa_bwd_validation(lib):
     assert _nbwd(lib, dq=P + 8) == EALIGN
     assert _nbwd(lib, B=0, q=None, k=None, v=None, idx=None, o=None, lse=None, do=None,
                  dq=None, dk=None, dv=None, ws=None) == OK
+
+
+def _fsa(lib, q=P, k=P, v=P, idx=P, o=P, lse=P, ws=P, wsb=1 << 40, B=1, Hq=8, Hkv=2, T=128,
+         D=128, bs=64, S=4):
+    return lib.nsa_sel_fwd_fsa(q, k, v, idx, o, lse, ws, wsb, B, Hq, Hkv, T, D, bs, S, None)
+
+
+def test_nsa_fsa_validation(lib):
+    small = lib.nsa_sel_fsa_workspace_bytes(1, 8, 2, 128, 128, 64, 4)
+    assert small > 0
+    assert lib.nsa_sel_fsa_workspace_bytes(1, 8, 2, 1024, 128, 64, 4) > small
+    assert lib.nsa_sel_fsa_workspace_bytes(1, 8, 2, 100, 128, 64, 4) == 0   # T % bs
+    assert _fsa(lib, o=None) == ENULL
+    assert _fsa(lib, idx=None) == ENULL
+    assert _fsa(lib, D=96) == EUNSUP
+    assert _fsa(lib, bs=48, T=96) == EUNSUP
+    assert _fsa(lib, S=65) == EUNSUP
+    assert _fsa(lib, Hq=34, Hkv=2) == EUNSUP
+    assert _fsa(lib, T=100) == ESHAPE
+    assert _fsa(lib, ws=None) == EWORK
+    assert _fsa(lib, wsb=small - 1) == EWORK
+    assert _fsa(lib, ws=P + 64) == EALIGN
+    assert _fsa(lib, o=P + 8) == EALIGN
+    assert _fsa(lib, lse=P + 2) == EALIGN
+    assert _fsa(lib, Hq=64, Hkv=4, T=131072) == EUNSUP   # q rows past 32-bit offsets
+    assert _fsa(lib, B=0, q=None, k=None, v=None, idx=None, o=None, lse=None, ws=None) == OK
 
 
 def test_binding_refuses_cpu_tensors(lib):
