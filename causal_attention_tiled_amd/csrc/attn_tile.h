@@ -120,6 +120,29 @@ __device__ __forceinline__ void tr_read4x2(bf16x4_t (&r)[8], const uint32_t (&ad
         : "memory");
 }
 
+// Eight 16-byte LDS reads (ds_read_b128): r[2k] at LDS byte address addr[k], r[2k+1]
+// at addr[k] + OFF, after s_waitcnt vmcnt(VM) and ending with lgkmcnt(0), in one
+// statement (as tr_read4x2, for row-major operand reads of a DMA'd tile).
+template <int VM, int OFF>
+__device__ __forceinline__ void row_read4x2(u32x4 (&r)[8], const uint32_t (&addr)[4]) {
+    static_assert(VM >= 0 && VM < 64 && OFF >= 0 && OFF < 65536, "immediates");
+    asm volatile(
+        "s_waitcnt vmcnt(%12)\n\t"
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%13\n\t"
+        "ds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %9 offset:%13\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %10 offset:%13\n\t"
+        "ds_read_b128 %6, %11\n\t"
+        "ds_read_b128 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+          "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "n"(VM), "n"(OFF)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }

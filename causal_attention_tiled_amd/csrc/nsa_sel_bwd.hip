@@ -58,12 +58,14 @@ __device__ __forceinline__ void bwd_dma16(__amdgpu_buffer_rsrc_t r, void *lds, i
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, soff, 0, 0);
 }
 
-// LDS K chunk (32 rows x D*2 bytes) swizzle for the transposing reads (as the
-// forward's V tile): chunk c of row r at slot c ^ swz(r).
+// LDS K chunk (32 rows x D*2 bytes): 16-byte piece c of row r at slot c ^ swz(r).  At
+// D = 128 (one row per 256-byte bank line) the 16 rows x 16 bytes that 16 lanes read
+// for the K operand, and the 8 rows x 32 bytes that 32 lanes read transposed for the
+// K^T operand, each cover all 64 banks once.
 template <int D>
 __host__ __device__ constexpr int chunk_swz(int row) {
     if constexpr (D == 128)
-        return (row & 7) << 1;
+        return ((row & 7) << 1) | ((row >> 3) & 1);
     else
         return ((row >> 1) & 3) << 1;
 }
@@ -162,22 +164,23 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     }
 
     typedef uint8_t KTileBuf[kDqWaves][KTILE];
-    bf16x8 kfa[2][NDS], vfa[2][NDS], kfb[2][NDS], vfb[2][NDS];
-    auto load_rows = [&](int k0, bf16x8 (&kf)[2][NDS], bf16x8 (&vf)[2][NDS]) {
+    // K rows as A operands of S^T, read from the LDS copy: row 16*kk + n16, dims
+    // 32*ds + 8*g4 (the kk = 1 rows 16 rows further, same swizzle)
+    int krow_off[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+        krow_off[ds] = n16 * ROWB + (((4 * ds + g4) ^ chunk_swz<D>(n16)) << 4);
+
+    // V rows in registers (A operands of dP^T); K only through the LDS copy
+    bf16x8 vfa[2][NDS], vfb[2][NDS];
+    auto load_chunk = [&](int k0, bf16x8 (&vf)[2][NDS], KTileBuf &kt) {  // 2*NDS + KDMA ops
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) {
-                kf[kk][ds] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + ds * 64,
-                                                                  (k0 + 16 * kk) * ROWB, 0));
+            for (int ds = 0; ds < NDS; ++ds)
                 vf[kk][ds] = __builtin_bit_cast(
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, koff + ds * 64,
                                                                   (k0 + 16 * kk) * ROWB, 0));
-            }
-    };
-    auto load_chunk = [&](int k0, bf16x8 (&kf)[2][NDS], bf16x8 (&vf)[2][NDS], KTileBuf &kt) {
-        load_rows(k0, kf, vf);
 #pragma unroll
         for (int j = 0; j < KDMA; ++j) bwd_dma16(rk, &kt[wave][j * 1024], kdma_off[j], k0 * ROWB);
     };
@@ -217,10 +220,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     float dl = 0.0f;  // this lane's part of delta
     // VM: memory instructions issued after this chunk's K transfer (the next chunk's, or
     // none): the K^T reads wait for exactly this chunk's DMA.
-    constexpr int NEXT_OPS = 4 * NDS + KDMA;
-    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const bf16x8 (&vf)[2][NDS],
-                             const KTileBuf &kt, auto vm) {
+    constexpr int NEXT_OPS = 2 * NDS + KDMA;
+    auto compute_chunk = [&](int k0, const bf16x8 (&vf)[2][NDS], const KTileBuf &kt, auto vm) {
         constexpr int VM = decltype(vm)::value;
+        const uint32_t base = lds_addr(&kt[wave][0]);
+        bf16x8 kf[2][NDS];
+        {
+            static_assert(NDS == 4 || NDS == 2, "K row reads");
+            uint32_t ad[4];
+            u32x4 rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + krow_off[e % NDS];
+            row_read4x2<VM, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                kf[0][ds] = as_bf16x8(rd[2 * ds]);
+                kf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
+            }
+        }
         f32x4 pr[2], dp[2];
         scores(k0, kf, vf, pr, dp);
         bf16x8 xf, yf;
@@ -232,18 +249,14 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
                 xf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - m));
                 yf[kk * 4 + j] = (__bf16)pr[kk][j];
             }
-        // X^T += K^T xf^T, Y^T += K^T yf^T
-        const uint32_t base = lds_addr(&kt[wave][0]);
+        // X^T += K^T xf^T, Y^T += K^T yf^T (the tile is already in: no vmcnt wait)
 #pragma unroll
         for (int d4 = 0; d4 < NDT; d4 += 4) {
             uint32_t ad[4];
             bf16x4_t rd[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ad[e] = base + krd_off[d4 + e];
-            if (d4 == 0)
-                tr_read4x2<VM, 16 * ROWB>(rd, ad);
-            else
-                tr_read4x2<63, 16 * ROWB>(rd, ad);
+            tr_read4x2<63, 16 * ROWB>(rd, ad);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bf16x8 kt8 = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3,
@@ -270,26 +283,26 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         return cur_blk * BS;
     };
 
-    // chunks alternate between (kfa, vfa, kbuf_a) and (kfb, vfb, kbuf_b), each fetched
-    // one chunk ahead; a chunk's K^T reads are complete when compute_chunk returns, so
-    // its tile may be refilled right after
+    // chunks alternate between (vfa, kbuf_a) and (vfb, kbuf_b), each fetched one chunk
+    // ahead; a chunk's LDS reads are complete when compute_chunk returns, so its tile
+    // may be refilled right after
     int ka = next_chunk();
-    if (ka >= 0) load_chunk(ka, kfa, vfa, kbuf_a);
+    if (ka >= 0) load_chunk(ka, vfa, kbuf_a);
     int kb = ka >= 0 ? next_chunk() : -1;
     while (ka >= 0) {
         if (kb >= 0) {
-            load_chunk(kb, kfb, vfb, kbuf_b);
-            compute_chunk(ka, kfa, vfa, kbuf_a, next_loaded{});
+            load_chunk(kb, vfb, kbuf_b);
+            compute_chunk(ka, vfa, kbuf_a, next_loaded{});
         } else {
-            compute_chunk(ka, kfa, vfa, kbuf_a, none_loaded{});
+            compute_chunk(ka, vfa, kbuf_a, none_loaded{});
             break;
         }
         ka = next_chunk();
         if (ka >= 0) {
-            load_chunk(ka, kfa, vfa, kbuf_a);
-            compute_chunk(kb, kfb, vfb, kbuf_b, next_loaded{});
+            load_chunk(ka, vfa, kbuf_a);
+            compute_chunk(kb, vfb, kbuf_b, next_loaded{});
         } else {
-            compute_chunk(kb, kfb, vfb, kbuf_b, none_loaded{});
+            compute_chunk(kb, vfb, kbuf_b, none_loaded{});
         }
         kb = ka >= 0 ? next_chunk() : -1;
     }
