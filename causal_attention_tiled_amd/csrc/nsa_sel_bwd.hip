@@ -359,13 +359,13 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     __shared__ __attribute__((aligned(16))) int rpos[NBUF][32];
     __shared__ int qpos[kNsaSegQ];
 
-    // workgroup -> segment: each XCD takes a contiguous range of segments (lists in
-    // (group, block) order, so the heavily attended early blocks come first)
+    // workgroup -> segment in list order (group, then block): the workgroups in flight
+    // work on one kv group at a time, whose gathered q rows (G*T rows per group) are
+    // then the working set of the memory-side cache, and the heavily attended early
+    // blocks of each group come first
     const int seg_total = seg_start[nlists];
-    const int per = (seg_total + 7) >> 3;
-    const int wgi = blockIdx.x >> 3;
-    const int sidx = (blockIdx.x & 7) * per + wgi;
-    if (wgi >= per || sidx >= seg_total) return;  // whole workgroup: before any barrier
+    const int sidx = blockIdx.x;
+    if (sidx >= seg_total) return;  // whole workgroup, before any barrier
     const int l = __builtin_amdgcn_readfirstlane(seg_list[sidx]);
     const int seg = sidx - seg_start[l];
     const bool multi = seg_start[l + 1] - seg_start[l] > 1;
