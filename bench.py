@@ -82,11 +82,20 @@ def nsa_gathered_bytes(idx, T, bs, D, rows_kv=None):
 
 
 def kernel_source_hash(name):
+    """Hash of the kernel's sources and the build script; in the C/HIP files, // comments
+    and blank lines are left out, so an edit of a comment keeps a measurement valid and
+    any edit of code invalidates it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[name] + ["../build.py"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+            data = fh.read()
+        if not f.endswith(".py"):
+            text = data.decode()
+            lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+            data = "\n".join(ln for ln in lines if ln).encode()
+        h.update(data)
     return h.hexdigest()[:16]
 
 

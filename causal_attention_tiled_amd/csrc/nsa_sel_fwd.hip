@@ -28,7 +28,10 @@
 //  * The exponentials, rounded to bf16, form in accumulator register order the B
 //    operand of O^T += V^T P^T; the V^T operand is read from the row-major LDS tile
 //    with ds_read_b64_tr_b16 (in each 16-lane group, output lane i, value t is
-//    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).
+//    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).  Those reads
+//    sit in one statement with an s_waitcnt vmcnt that awaits exactly this chunk's V
+//    transfer (the next chunk's loads stay in flight); the compiler's own wait for
+//    DMA'd LDS data would be vmcnt(0).
 //  * Workgroup order keeps each XCD on a contiguous range of (group, query) work so a
 //    group's K/V stays in one XCD's L2.
 #include <type_traits>
