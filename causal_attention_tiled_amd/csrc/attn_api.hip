@@ -58,6 +58,13 @@ int nsa_validate(const void *q, const void *k, const void *v, const int32_t *blo
     return ATTN_OK;
 }
 
+// The inverted selection (block-outer NSA kernels) keeps list positions in int32: the
+// number of (group, query, block) entries it may hold must stay below 2^31.
+bool nsa_index_fits(int B, int Hkv, int T, int block_size, int S) {
+    const int64_t nblk = T / block_size;
+    return (int64_t)B * Hkv * T * (S < nblk ? S : nblk) < ((int64_t)1 << 31);
+}
+
 }  // namespace
 
 ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, int B, int H,
@@ -166,6 +173,7 @@ ATTN_EXPORT int nsa_sel_bwd(const void *q, const void *k, const void *v,
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
     // per-batch byte offsets of q / dout rows must fit the 32-bit buffer addressing
     if ((int64_t)Hq * T * D * 2 >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    if (!nsa_index_fits(B, Hkv, T, block_size, S)) return ATTN_ERR_UNSUPPORTED;
     const size_t need = attn::nsa_sel_bwd_workspace(B, Hq, Hkv, T, D, block_size, S);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;
@@ -198,6 +206,7 @@ ATTN_EXPORT int nsa_sel_fwd_fsa(const void *q, const void *k, const void *v,
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
     // per-batch byte offsets of q rows must fit the 32-bit buffer addressing
     if ((int64_t)Hq * T * D * 2 >= (int64_t)1 << 31) return ATTN_ERR_UNSUPPORTED;
+    if (!nsa_index_fits(B, Hkv, T, block_size, S)) return ATTN_ERR_UNSUPPORTED;
     const size_t need = attn::nsa_sel_fsa_workspace(B, Hq, Hkv, T, D, block_size, S);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_ALIGN;

@@ -208,8 +208,8 @@ int nsa_sel_fwd(const void *q, const void *k, const void *v, const int32_t *bloc
  *                  nsa_sel_bwd_workspace_bytes(...) bytes, 256-byte aligned (else
  *                  ATTN_ERR_WORKSPACE / ATTN_ERR_ALIGN).  Calls that share one
  *                  workspace must not overlap in time.
- *   sizes        : as nsa_sel_fwd; in addition Hq*T*D*2 < 2^31 (else
- *                  ATTN_ERR_UNSUPPORTED).
+ *   sizes        : as nsa_sel_fwd; in addition Hq*T*D*2 < 2^31 and
+ *                  B*Hkv*T*min(S, T/block_size) < 2^31 (else ATTN_ERR_UNSUPPORTED).
  *
  * Numerics: scores, dP and delta in fp32 from bf16 products.  delta is summed
  * from the recomputed probabilities; dout . out (out is bf16) serves only as an
@@ -243,7 +243,8 @@ size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int blo
  *               ATTN_ERR_WORKSPACE / ATTN_ERR_ALIGN); it holds the inverted
  *               selection and one partial per (query, selected block, head).
  *               Calls that share one workspace must not overlap in time.
- *   sizes     : in addition Hq*T*D*2 < 2^31 (else ATTN_ERR_UNSUPPORTED).
+ *   sizes     : in addition Hq*T*D*2 < 2^31 and B*Hkv*T*min(S, T/block_size)
+ *               < 2^31 (else ATTN_ERR_UNSUPPORTED).
  *
  * Numerics: scores fp32 from bf16 products; per block the row max, sum and
  * weighted sum in fp32, probabilities rounded to bf16 before they multiply V,

@@ -186,6 +186,9 @@ def test_nsa_fsa_validation(lib):
     assert _fsa(lib, o=P + 8) == EALIGN
     assert _fsa(lib, lse=P + 2) == EALIGN
     assert _fsa(lib, Hq=64, Hkv=4, T=131072) == EUNSUP   # q rows past 32-bit offsets
+    # more (group, query, block) entries than int32 list positions hold
+    assert _fsa(lib, B=1024, Hq=16, Hkv=16, T=8192, D=64, bs=32, S=64) == EUNSUP
+    assert _nbwd(lib, B=1024, Hq=16, Hkv=16, T=8192, D=64, bs=32, S=64) == EUNSUP
     assert _fsa(lib, B=0, q=None, k=None, v=None, idx=None, o=None, lse=None, ws=None) == OK
 
 
