@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     uint16_t *__restrict__ dV, int Hq, int Hkv, int G, int T, int nblk, int nlists,
     float score_scale, float scale) {
     constexpr int NW = BS / 32;                  // one wave per 32 keys of the block
-    constexpr int NBUF = BS == 32 ? 2 : 4;       // staged chunks (ring)
+    constexpr int NBUF = BS == 32 ? 3 : 4;       // staged chunks (ring)
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
     constexpr int TILEB = 32 * ROWB;             // 32 gathered rows of one tensor
@@ -423,16 +423,20 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     // OPS memory instructions per wave: LOADS for Q, LOADS for dO, lse, delta.  Row r of
     // chunk c is query qpos[c*qc + r/G], head kv*G + r%G; absent rows read as zero.
     auto stage = [&](int c, int u) {
+        int off[LOADS];  // all query positions read first (one LDS wait), then the DMAs
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             const int r = srow[j];
             const int qi = c * qc + r / G;
-            int off = (int)bbytes;
-            if (r < rows_used && qi < nq)
-                off = ((kv * G + r % G) * T + qpos[qi]) * ROWB + (sslot[j] << 4);
+            const bool ok = r < rows_used && qi < nq;
+            const int pos = qpos[ok ? qi : 0];  // c < nchunks, so nq > 0
+            off[j] = ok ? ((kv * G + r % G) * T + pos) * ROWB + (sslot[j] << 4) : (int)bbytes;
+        }
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
             const int dst = (wave * LOADS + j) * 1024;
-            dma16(rq, &lds[(2 * u) * TILEB + dst], off, 0);
-            dma16(ro, &lds[(2 * u + 1) * TILEB + dst], off, 0);
+            dma16(rq, &lds[(2 * u) * TILEB + dst], off[j], 0);
+            dma16(ro, &lds[(2 * u + 1) * TILEB + dst], off[j], 0);
         }
         if (lane < 32) {  // every wave writes the same table entries
             const int qi = c * qc + lane / G;
@@ -462,15 +466,12 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
                           (((4 * dt + 2 * (g16 & 1) + ((s16 & 3) >> 1)) ^ tile_swz<D>(row)) << 4) +
                           8 * (s16 & 1);
         }
-    auto row_frag = [&](int tile, int ds) {
-        return *(const bf16x8 *)(&lds[tile * TILEB + roff[ds]]);
-    };
-    auto t_frag = [&](int tile, int dt, int c) {
-        const uint8_t *p = &lds[tile * TILEB + 16 * c * ROWB];
-        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][0]));
-        const bf16x4_t up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p + toff[dt][1]));
-        return (bf16x8)__builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
+    // LDS operand reads are issued in groups of eight per statement (tr_read4x2,
+    // row_read4x2), so one wait covers eight reads and the products of a group run while
+    // the next group is read.  Chunk tiles are complete before any of them (waited and
+    // published by the barrier), hence vmcnt(63): no memory wait inside.
+    const uint32_t lds0 = lds_addr(&lds[0]);
+    static_assert(NDS % 4 == 0 && NDT % 2 == 0, "operand read groups");
 
     f32x16 dkacc[NDT], dvacc[NDT];
 #pragma unroll
@@ -487,28 +488,54 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
     __syncthreads();  // qpos
     for (int c = 0; c < NBUF - 1 && c < nchunks; ++c) stage(c, c);
 
-    for (int c = 0; c < nchunks; ++c) {
-        const int u = c % NBUF;
-        // chunk c's transfers are done once at most (chunks staged after it) * OPS remain
-        const int after = min(NBUF - 2, nchunks - 1 - c);
-        if constexpr (NBUF == 4) {
-            if (after >= 2) wait_vm<2 * OPS>();
-            else if (after == 1) wait_vm<OPS>();
-            else wait_vm<0>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();  // every wave's part of chunk c is in; chunk c-1 is consumed
-        if (c + NBUF - 1 < nchunks) stage(c + NBUF - 1, (c + NBUF - 1) % NBUF);
-
-        // register r: row m = 8*(r/4) + 4*hi + r%4 of the chunk, key mykey (lane)
-        f32x16 s = zero16, dp = zero16;
+    // S = Q K^T and dP = dO V^T of chunk c (register r: row m = 8*(r/4) + 4*hi + r%4 of
+    // the chunk, key mykey), then P and dS rounded to bf16 in the register order of the
+    // B operands of dV^T += dO^T P and dK^T += Q^T dS
+    auto scores = [&](int u, f32x16 &s, f32x16 &dp) {
+        s = zero16;
+        dp = zero16;
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-            s = mfma_32x32x16(row_frag(2 * u, ds), kf[ds], s);
-            dp = mfma_32x32x16(row_frag(2 * u + 1, ds), vf[ds], dp);
+        for (int d4 = 0; d4 < NDS; d4 += 4) {
+            uint32_t ad[4];
+            u32x4 rd[8];  // rd[2e]: Q row piece d4+e, rd[2e+1]: the dO row piece
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = lds0 + 2 * u * TILEB + roff[d4 + e];
+            row_read4x2<63, TILEB>(rd, ad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s = mfma_32x32x16(as_bf16x8(rd[2 * e]), kf[d4 + e], s);
+                dp = mfma_32x32x16(as_bf16x8(rd[2 * e + 1]), vf[d4 + e], dp);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8 pb[2], sb[2];
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS for chunk tile u
+    auto products = [&](int u, const bf16x8 (&pb)[2], const bf16x8 (&sb)[2]) {
+#pragma unroll
+        for (int d2 = 0; d2 < NDT; d2 += 2)
+#pragma unroll
+            for (int t = 1; t >= 0; --t) {  // dO^T (dV) then Q^T (dK)
+                uint32_t ad[4];
+                bf16x4_t rd[8];  // rd[4e + 2h + c]: dim tile d2+e, half h, key group c
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) ad[2 * e + h] = lds0 + (2 * u + t) * TILEB + toff[d2 + e][h];
+                tr_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const bf16x8 a = __builtin_shufflevector(rd[4 * e + c], rd[4 * e + 2 + c], 0, 1,
+                                                                 2, 3, 4, 5, 6, 7);
+                        if (t == 1) dvacc[d2 + e] = mfma_32x32x16(a, pb[c], dvacc[d2 + e]);
+                        else dkacc[d2 + e] = mfma_32x32x16(a, sb[c], dkacc[d2 + e]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
+    auto weights = [&](int u, const f32x16 &s, const f32x16 &dp, bf16x8 (&pb)[2],
+                       bf16x8 (&sb)[2]) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 ls = *(const f32x4 *)(&rlse[u][8 * g + 4 * hi]);
@@ -523,13 +550,44 @@ __global__ __launch_bounds__(64 * (BS / 32)) void nsa_bwd_dkv_kernel(
                 sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - de[j]));
             }
         }
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                dvacc[dt] = mfma_32x32x16(t_frag(2 * u + 1, dt, cc), pb[cc], dvacc[dt]);
-                dkacc[dt] = mfma_32x32x16(t_frag(2 * u, dt, cc), sb[cc], dkacc[dt]);
-            }
+    };
+    // wait until chunk c's transfers are in; the chunks staged after it may still be
+    // outstanding, OPS instructions each: before the loop (c = 0) chunks 1 .. NBUF-2, and
+    // when iteration c-1 waits for chunk c, chunks c+1 .. c+NBUF-3
+    auto wait_chunk = [&](int c) {
+        const int after = c > 0 ? min(NBUF - 3, nchunks - 1 - c) : min(NBUF - 2, nchunks - 1);
+        if constexpr (NBUF >= 4) {
+            if (after >= 2) wait_vm<2 * OPS>();
+            else if (after == 1) wait_vm<OPS>();
+            else wait_vm<0>();
+        } else {
+            if (after >= 1) wait_vm<OPS>();
+            else wait_vm<0>();
+        }
+    };
+
+    // Software pipeline over chunks: iteration c issues S and dP of chunk c+1, then the
+    // dV/dK products of chunk c, then the weights of chunk c+1 (VALU work that runs while
+    // chunk c's products occupy the matrix unit).
+    bf16x8 pb[2], sb[2];
+    if (nchunks > 0) {
+        wait_chunk(0);
+        __syncthreads();
+        f32x16 s, dp;
+        scores(0, s, dp);
+        weights(0, s, dp, pb, sb);
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        const int u = c % NBUF, un = (c + 1) % NBUF;
+        const bool more = c + 1 < nchunks;
+        if (more) wait_chunk(c + 1);
+        __syncthreads();  // chunk c+1 is in for every wave; chunk c-1 is consumed
+        f32x16 s, dp;
+        if (more) scores(un, s, dp);
+        products(u, pb, sb);
+        // staged behind the products, so its LDS reads and address work overlap them
+        if (c + NBUF - 1 < nchunks) stage(c + NBUF - 1, (c + NBUF - 1) % NBUF);
+        if (more) weights(un, s, dp, pb, sb);
     }
 
     if (mykey >= T) return;

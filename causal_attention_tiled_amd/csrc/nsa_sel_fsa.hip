@@ -123,15 +123,17 @@ __global__ __launch_bounds__(64 * kFsaWaves) void nsa_fsa_partial_kernel(
         sslot[j] = ((pos % ROWB) >> 4) ^ tile_swz<D>(pos / ROWB);
     }
     auto stage = [&](int c, int u) {  // QLOADS memory instructions
+        int off[QLOADS];  // all query positions read first (one LDS wait), then the DMAs
 #pragma unroll
         for (int j = 0; j < QLOADS; ++j) {
             const int r = srow[j];
             const int qi = c * qc + r / G;
-            int off = (int)qbytes;
-            if (r < rows_used && qi < nq)
-                off = ((kv * G + r % G) * T + qpos[qi]) * ROWB + (sslot[j] << 4);
-            dma16(rq, &qt[wave][u][j * 1024], off, 0);
+            const bool ok = r < rows_used && qi < nq;
+            const int pos = qpos[ok ? qi : 0];  // c < nchunks, so nq > 0
+            off[j] = ok ? ((kv * G + r % G) * T + pos) * ROWB + (sslot[j] << 4) : (int)qbytes;
         }
+#pragma unroll
+        for (int j = 0; j < QLOADS; ++j) dma16(rq, &qt[wave][u][j * 1024], off[j], 0);
         if (lane < 32) {
             const int qi = c * qc + lane / G;
             rpos[wave][u][lane] = (lane < rows_used && qi < nq) ? qpos[qi] : -1;
