@@ -317,8 +317,9 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, int T, int nqt, float beta, float p) {
     constexpr int BQ = kTraF32Rows, BK = 64, DPT = D / 4;
-    __shared__ float Ksh[BK][D];
-    __shared__ float Vsh[BK][D];
+    static_assert(BK % 4 == 0, "four keys per step");
+    __shared__ __attribute__((aligned(16))) float Ksh[BK][D];
+    __shared__ __attribute__((aligned(16))) float Vsh[BK][D];
 
     const int bh = blockIdx.x / nqt;
     const int qt = nqt - 1 - blockIdx.x % nqt;
@@ -336,25 +337,54 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const float tau = beta * sqrtf(2.0f * logf((float)(my_q + 1)) / (float)D);
     const int q_last = min(qt * BQ + BQ, T) - 1;
 
+    // K/V tile staging: 16-byte pieces, all of a thread's loads issued before its LDS
+    // stores (one memory latency per tile), and the next tile's loads issued before the
+    // current tile is computed
+    constexpr int PER = BK * D / 4 / kThreads;  // float4 pieces per thread per tensor
+    static_assert(BK * D % (4 * kThreads) == 0, "tile staging");
+    float4 kr[PER], vr[PER];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (tid + i * kThreads) * 4;
+            const int key = k0 + e / D;
+            const float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            kr[i] = key < T ? *(const float4 *)(K + slab + (size_t)key * D + e % D) : z;
+            vr[i] = key < T ? *(const float4 *)(V + slab + (size_t)key * D + e % D) : z;
+        }
+    };
+    fetch(0);
     for (int k0 = 0; k0 <= q_last; k0 += BK) {
         __syncthreads();
-        for (int e = tid; e < BK * D; e += kThreads) {
-            const int row = e / D, col = e % D, key = k0 + row;
-            Ksh[row][col] = key < T ? K[slab + (size_t)key * D + col] : 0.0f;
-            Vsh[row][col] = key < T ? V[slab + (size_t)key * D + col] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = (tid + i * kThreads) * 4;
+            *(float4 *)(&Ksh[e / D][e % D]) = kr[i];
+            *(float4 *)(&Vsh[e / D][e % D]) = vr[i];
         }
         __syncthreads();
+        if (k0 + BK <= q_last) fetch(k0 + BK);
+        // four keys per step: four independent dot-product chains (the same summation
+        // order per key as one at a time), then the weighted rows added in key order;
+        // keys past the row (or past the tile's last row) get weight 0
         const int jn = min(BK, q_last - k0 + 1);
-        for (int j = 0; j < jn; ++j) {
-            float s = 0.0f;
+        for (int j = 0; j < jn; j += 4) {
+            float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int d = 0; d < DPT; ++d) s = fmaf(qv[d], Ksh[j][part * DPT + d], s);
-            s += __shfl_xor(s, 1);
-            s += __shfl_xor(s, 2);
-            float w = relu_pow<PM>(s - tau, p);
-            if (k0 + j > my_q) w = 0.0f;
+            for (int d = 0; d < DPT; ++d)
 #pragma unroll
-            for (int d = 0; d < DPT; ++d) acc[d] = fmaf(w, Vsh[j][part * DPT + d], acc[d]);
+                for (int u = 0; u < 4; ++u) sc[u] = fmaf(qv[d], Ksh[j + u][part * DPT + d], sc[u]);
+            float w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float x = sc[u] + __shfl_xor(sc[u], 1);
+                x += __shfl_xor(x, 2);
+                w[u] = k0 + j + u > my_q ? 0.0f : relu_pow<PM>(x - tau, p);
+            }
+#pragma unroll
+            for (int d = 0; d < DPT; ++d)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[d] = fmaf(w[u], Vsh[j + u][part * DPT + d], acc[d]);
         }
     }
     if (my_q < T) {
