@@ -17,8 +17,9 @@
 //  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
-//    order, and dQ^T += K^T (.)^T with K^T read transposed from a per-wave LDS copy
-//    of the chunk.  delta is needed before the first dS and is only known after the
+//    order, and dQ^T += K^T (.)^T.  V rows go to registers; K goes once into a
+//    per-wave LDS copy of the chunk that serves both the K operand (row reads) and K^T
+//    (transposing reads).  delta is needed before the first dS and is only known after the
 //    last key, and dout . out from the forward's bf16 output is too coarse a value for
 //    dP - delta, which cancels.  So one pass accumulates, against the estimate
 //    m = dout . out, X = sum_j bf16(P_j (dP_j - m)) k_j, Y = sum_j bf16(P_j) k_j and
@@ -29,9 +30,11 @@
 //  * dk/dv: one workgroup per segment of a (group, block) list, one wavefront per 32
 //    keys of the block holding its K and V rows in registers, the segment's queries
 //    walked in chunks of 32 rows (query, head): their Q and dO rows are gathered into
-//    LDS by the memory unit, four chunks ahead, with lse, delta and position in a
-//    small table.  S = Q K^T and dP = dO V^T (one key per lane), then dV^T += dO^T P
-//    and dK^T += Q^T dS with dO^T and Q^T read transposed from LDS.  A list of one
+//    LDS by the memory unit, up to three chunks ahead, with lse, delta and position in
+//    a small table.  S = Q K^T and dP = dO V^T (one key per lane), then dV^T += dO^T P
+//    and dK^T += Q^T dS with dO^T and Q^T read transposed from LDS; the chunk loop is
+//    software-pipelined (S and dP of the next chunk are issued before this chunk's
+//    products, its weights after them).  A list of one
 //    segment writes its key rows; a longer list writes fp32 partials that a reduce
 //    kernel sums in segment order.  Each key row has one writer: deterministic.
 #include <algorithm>
