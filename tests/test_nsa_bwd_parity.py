@@ -53,6 +53,22 @@ def test_nsa_bwd_small(gpu, cfg):
         assert_rows_close(g, r, BF16_REL, f"{n} {cfg}", floor=FLOOR)
 
 
+def test_nsa_bwd_S64_max_slots(gpu):
+    """S = 64, the most slots (one per lane), selecting every causal block: dq on every
+    row, dk and dv on sampled key rows (the oracle's key-row gradients sum over every
+    query and head, so all 4096 would take minutes)."""
+    B, Hq, Hkv, T, D, bs, S = 1, 4, 2, 2048, 64, 32, 64
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=64)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=64)
+    do = _dout((B, Hq, T, D), seed=65)
+    dq, dk, dv = _run(q, k, v, idx, bs, do, gpu)
+    krows = sample_rows(B, Hkv, T, 24, seed=66, extra_positions=(0, 31, 32, 1023, 2047))
+    rq, rk, rv = oracle.nsa_bwd_ref(q, k, v, idx, bs, do, krows=krows)
+    assert_rows_close(dq, rq, BF16_REL, "dq S64", floor=FLOOR)
+    assert_rows_close(dk.reshape(-1, D)[krows], rk, BF16_REL, "dk S64", floor=FLOOR)
+    assert_rows_close(dv.reshape(-1, D)[krows], rv, BF16_REL, "dv S64", floor=FLOOR)
+
+
 def test_nsa_bwd_edge_blocks(gpu):
     """Duplicates, out-of-range ids, padding-only rows and unselected blocks."""
     B, Hq, Hkv, T, D, bs, S = 1, 4, 2, 256, 128, 32, 6

@@ -31,6 +31,7 @@ SMALL = [  # B, Hq, Hkv, T, D, bs, S
     (1, 6, 2, 256, 128, 128, 2),    # block 128, G = 3
     (1, 3, 1, 64, 64, 64, 1),       # one block, S = 1
     (2, 10, 2, 320, 64, 32, 16),    # G = 5, many slots
+    (1, 4, 2, 2048, 64, 32, 64),    # S = 64, the most slots (one per lane): every block
 ]
 
 
