@@ -46,7 +46,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Query rows per workgroup of the bf16 / fp32 Threshold Rectified Attention kernels.
 constexpr int kTraBf16Rows = 256;
-constexpr int kTraF32Rows = 64;
+constexpr int kTraF32Rows = 16;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;
 // Query rows (dq kernel) and key rows (dk/dv kernel) per workgroup of the

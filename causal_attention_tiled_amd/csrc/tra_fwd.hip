@@ -310,14 +310,19 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     }
 }
 
-// fp32 kernel: 64 query rows per workgroup, 4 lanes per row (each a quarter of the
-// head dim), K/V tiles of 64 keys staged in LDS, all arithmetic in fp32.
+// fp32 kernel: 16 query rows per workgroup; each wave takes one quarter of every key
+// tile for all 16 rows (4 lanes per row, each a quarter of the head dim), and the four
+// partial outputs are summed through LDS at the end.  K/V tiles of 64 keys are staged
+// in LDS; all arithmetic is fp32.
 template <int D, int PM>
 __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, int T, int nqt, float beta, float p) {
     constexpr int BQ = kTraF32Rows, BK = 64, DPT = D / 4;
-    static_assert(BK % 4 == 0, "four keys per step");
+    constexpr int NSL = kThreads / (BQ * 4);     // key slices (waves) per workgroup
+    constexpr int KS = BK / NSL;                 // keys of a tile per slice
+    static_assert(NSL * BQ * 4 == kThreads && KS % 4 == 0, "slices");
+    static_assert(NSL * BQ * D <= BK * D, "the reduction reuses the K tile");
     __shared__ __attribute__((aligned(16))) float Ksh[BK][D];
     __shared__ __attribute__((aligned(16))) float Vsh[BK][D];
 
@@ -325,7 +330,9 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const int qt = nqt - 1 - blockIdx.x % nqt;
     const int tid = threadIdx.x;
     const int part = tid & 3;
-    const int my_q = qt * BQ + (tid >> 2);
+    const int row = (tid >> 2) % BQ;
+    const int slice = tid / (BQ * 4);
+    const int my_q = qt * BQ + row;
     const size_t slab = (size_t)bh * T * D;
 
     float qv[DPT], acc[DPT];
@@ -338,8 +345,7 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const int q_last = min(qt * BQ + BQ, T) - 1;
 
     // K/V tile staging: 16-byte pieces, all of a thread's loads issued before its LDS
-    // stores (one memory latency per tile), and the next tile's loads issued before the
-    // current tile is computed
+    // stores, and the next tile's loads issued before the current tile is computed
     constexpr int PER = BK * D / 4 / kThreads;  // float4 pieces per thread per tensor
     static_assert(BK * D % (4 * kThreads) == 0, "tile staging");
     float4 kr[PER], vr[PER];
@@ -364,32 +370,44 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
         }
         __syncthreads();
         if (k0 + BK <= q_last) fetch(k0 + BK);
-        // four keys per step: four independent dot-product chains (the same summation
-        // order per key as one at a time), then the weighted rows added in key order;
-        // keys past the row (or past the tile's last row) get weight 0
-        const int jn = min(BK, q_last - k0 + 1);
-        for (int j = 0; j < jn; j += 4) {
-            float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // this slice's keys, four per step: four independent dot-product chains, then
+        // the weighted rows added in key order; keys past the row get weight 0
+        const int j0 = slice * KS;
+        if (k0 + j0 <= q_last) {
+            for (int j = j0; j < j0 + KS; j += 4) {
+                float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int d = 0; d < DPT; ++d)
+                for (int d = 0; d < DPT; ++d)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) sc[u] = fmaf(qv[d], Ksh[j + u][part * DPT + d], sc[u]);
-            float w[4];
+                    for (int u = 0; u < 4; ++u) sc[u] = fmaf(qv[d], Ksh[j + u][part * DPT + d], sc[u]);
+                float w[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                float x = sc[u] + __shfl_xor(sc[u], 1);
-                x += __shfl_xor(x, 2);
-                w[u] = k0 + j + u > my_q ? 0.0f : relu_pow<PM>(x - tau, p);
+                for (int u = 0; u < 4; ++u) {
+                    float x = sc[u] + __shfl_xor(sc[u], 1);
+                    x += __shfl_xor(x, 2);
+                    w[u] = k0 + j + u > my_q ? 0.0f : relu_pow<PM>(x - tau, p);
+                }
+#pragma unroll
+                for (int d = 0; d < DPT; ++d)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[d] = fmaf(w[u], Vsh[j + u][part * DPT + d], acc[d]);
             }
-#pragma unroll
-            for (int d = 0; d < DPT; ++d)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) acc[d] = fmaf(w[u], Vsh[j + u][part * DPT + d], acc[d]);
         }
     }
-    if (my_q < T) {
+    // sum the slices' partial outputs (in slice order) through the K tile's LDS
+    __syncthreads();
+    float *red = &Ksh[0][0];  // [slice][row][D]
 #pragma unroll
-        for (int d = 0; d < DPT; ++d) O[slab + (size_t)my_q * D + part * DPT + d] = acc[d];
+    for (int d = 0; d < DPT; ++d) red[(slice * BQ + row) * D + part * DPT + d] = acc[d];
+    __syncthreads();
+    if (slice == 0 && my_q < T) {
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) {
+            float o = red[row * D + part * DPT + d];
+#pragma unroll
+            for (int sl = 1; sl < NSL; ++sl) o += red[(sl * BQ + row) * D + part * DPT + d];
+            O[slab + (size_t)my_q * D + part * DPT + d] = o;
+        }
     }
 }
 
