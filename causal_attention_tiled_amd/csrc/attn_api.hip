@@ -70,7 +70,7 @@ bool nsa_index_fits(int B, int Hkv, int T, int block_size, int S) {
 ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, int B, int H,
                         int T, int D, float beta, float p, void *stream) {
     bool noop;
-    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, attn::kTraBf16Rows, &noop);
+    const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, attn::tra_bf16_rows(D), &noop);
     if (st != ATTN_OK || noop) return st;
     const hipError_t e = attn::launch_tra_fwd_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),

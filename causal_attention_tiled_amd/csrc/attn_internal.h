@@ -44,8 +44,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Query rows per workgroup of the bf16 / fp32 Threshold Rectified Attention kernels.
-constexpr int kTraBf16Rows = 256;
+// Query rows per workgroup of the bf16 / fp32 Threshold Rectified Attention kernels
+// (bf16: 32 rows per wavefront; 8 wavefronts at D = 128, 4 at D = 64).
+constexpr int tra_bf16_waves(int D) { return D == 128 ? 8 : 4; }
+constexpr int tra_bf16_rows(int D) { return 32 * tra_bf16_waves(D); }
 constexpr int kTraF32Rows = 16;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;

@@ -5,8 +5,9 @@
 //     out_i = sum_{j <= i} max(q_i . k_j - tau_i, 0)^p v_j,   tau_i = beta*sqrt(2 ln(i+1) / D)
 // with a 0-based query position i, natural log, no 1/sqrt(D) scale and no softmax.
 //
-// bf16 kernel design (one workgroup = 8 wavefronts = 256 query rows of one (b,h),
-// two wavefronts per SIMD):
+// bf16 kernel design (one workgroup = 8 wavefronts = 256 query rows of one (b,h) at
+// D = 128, two wavefronts per SIMD; 4 wavefronts = 128 rows at D = 64, where two or
+// three workgroups share a compute unit):
 //  * Each wave owns 32 query rows.  It computes the TRANSPOSED score tile
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, K (A operand) from LDS, Q (B operand)
 //    held in registers for the whole key loop.  In the accumulator every lane then
@@ -22,6 +23,9 @@
 //  * Causal tile skipping: key tiles past the workgroup's last query are never loaded;
 //    tiles wholly after a wave's rows are skipped by that wave; the mask is evaluated
 //    only on tiles that reach past a wave's first row.
+//  * The wave issuing the second score block and the first epilogue runs at raised
+//    issue priority, so that of two waves on a SIMD the one with the mixed MFMA and
+//    VALU phase goes first.
 //  * Launch order: the heaviest query tiles (largest i) first, and the heads split
 //    into 8 contiguous groups so that each XCD (dispatch is round-robin over the 8
 //    XCDs) works on its own heads and keeps their K/V in its private L2.
@@ -34,8 +38,6 @@ namespace {
 
 constexpr int kThreads = 256;    // fp32 kernel
 constexpr int kQueryBlocks = 1;  // bf16 kernel: 32-row query blocks per wave
-constexpr int kWaves = 8;        // bf16 kernel: wavefronts per workgroup
-static_assert(kWaves * 32 * kQueryBlocks == kTraBf16Rows, "workgroup rows");
 constexpr int kBN = 64;   // keys per LDS tile
 
 template <int D, int PM, int QB, int NW>
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
             for (int qb = 0; qb < QB; ++qb) s0[qb] = mfma_32x32x16(ka[ds], qf[qb][ds], s0[qb]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMasked) mask_block(s0, n * kBN);
-        // B
+        // B (raised issue priority until C)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -243,6 +246,7 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMasked) mask_block(s1, n * kBN + 32);
         // C
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -414,10 +418,12 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
 template <int D, int PM>
 hipError_t launch_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *out,
                        int BH, int T, float beta, float p, hipStream_t stream) {
-    int nqt = (T + kTraBf16Rows - 1) / kTraBf16Rows;
+    constexpr int NW = tra_bf16_waves(D), ROWS = tra_bf16_rows(D);
+    static_assert(NW * 32 * kQueryBlocks == ROWS, "workgroup rows");
+    int nqt = (T + ROWS - 1) / ROWS;
     void *args[] = {&q, &k, &v, &out, &BH, &T, &nqt, &beta, &p};
-    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM, kQueryBlocks, kWaves>,
-                           dim3((unsigned)(BH * nqt)), dim3(64 * kWaves), args, 0, stream);
+    return hipLaunchKernel((const void *)tra_fwd_bf16_kernel<D, PM, kQueryBlocks, NW>,
+                           dim3((unsigned)(BH * nqt)), dim3(64 * NW), args, 0, stream);
 }
 
 template <int D, int PM>
