@@ -214,6 +214,8 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
     //   2: S2 = K2 Q2^T || S1 <- relu(S1 - tau)^p
     //   3: P = bf16(S1 - lam * relu(S2 - tau)^p)  (V operand read alongside)
     //   4: O += V P                            (next block's K1 operand read alongside)
+    // Phase 2 runs at raised issue priority: of two waves on a SIMD, the one in the
+    // mixed MFMA + VALU phase goes first.
     auto tile = [&](int n, auto masked, int buf) {
         constexpr bool kMasked = decltype(masked)::value;
         if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (kMasked) mask_block(s1, n * kBN + 32 * kb);
-            // 2
+            // 2 (raised issue priority until 3)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) s2 = mfma_32x32x16(k2f[ds], qf2[ds], s2);
 #pragma unroll
@@ -255,6 +258,7 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (kMasked) mask_block(s2, n * kBN + 32 * kb);
             // 3
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll

@@ -223,12 +223,14 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
             for (int qb = 0; qb < QB; ++qb) s0[qb] = mfma_32x32x16(ka[ds], qf[qb][ds], s0[qb]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMasked) mask_block(s0, n * kBN);
-        // B (raised issue priority until C)
-        __builtin_amdgcn_s_setprio(1);
+        // B (raised issue priority until C; at D = 128 only from the S1 products on,
+        // since raising it before the V operand reads makes the compiler spill)
+        if constexpr (D != 128) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int c = 0; c < 2; ++c) va[dt][c] = v_frag(buf, 0, dt, c);
+        if constexpr (D == 128) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s1[qb] = cinit[qb];
 #pragma unroll
