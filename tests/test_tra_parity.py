@@ -26,9 +26,11 @@ def _run_f32(q, k, v, beta, p, dev):
     return out.cpu()
 
 
-# several 128-row tiles, ragged tails, single rows, both head dims
+# several workgroup tiles (256 query rows at D=128, 128 at D=64), ragged tails, single
+# rows, both head dims; 128/129 and 256/257 sit on either side of a workgroup boundary
 SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 3, 127, 64), (1, 1, 129, 128),
-         (2, 2, 300, 128), (1, 2, 520, 64), (1, 1, 1000, 128)]
+         (1, 2, 128, 64), (1, 2, 129, 64), (1, 1, 256, 64), (2, 1, 257, 64), (1, 1, 256, 128),
+         (1, 1, 257, 128), (2, 2, 300, 128), (1, 2, 520, 64), (1, 1, 1000, 128)]
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
@@ -103,12 +105,13 @@ def test_tra_config_bf16_T8192_D128_sampled(gpu, big_tra):
     assert_rows_close(out.reshape(-1, D)[rows], ref, BF16_REL, "T8192 sampled")
 
 
-def test_tra_causality_bitexact(gpu):
+@pytest.mark.parametrize("D", [64, 128])
+def test_tra_causality_bitexact(gpu, D):
     """Changing K/V at positions > c must not change any output row <= c."""
-    B, H, T, D = 1, 2, 700, 128
+    B, H, T = 1, 2, 700
     q, k, v = inputs.tra_inputs(B, H, T, D, dtype=torch.bfloat16, seed=3)
     a = _run_bf16(q, k, v, 1.0, 2.0, gpu)
-    for c in (0, 63, 64, 200, 511):
+    for c in (0, 63, 64, 127, 128, 200, 255, 511):
         k2, v2 = k.clone(), v.clone()
         k2[:, :, c + 1:] = torch.randn_like(k2[:, :, c + 1:].float()).to(k.dtype) * 3
         v2[:, :, c + 1:] = torch.randn_like(v2[:, :, c + 1:].float()).to(v.dtype) * 3
