@@ -16,22 +16,28 @@
 //    holds slot s): padding, ids past T/bs, blocks after i and repeats of an earlier
 //    slot are dropped, and the survivors form a bit mask that the wave walks.  No
 //    scan over the KV sequence takes place.
-//  * Keys are processed in chunks of 32.  The next chunk is fetched while the
-//    current one is computed: its K rows go straight into the MFMA A-operand
-//    registers (buffer loads with a scalar chunk offset), its V rows are copied by
-//    the memory unit straight into one of two per-wave LDS tiles (two separate LDS
-//    objects, used alternately).
+//  * Keys are processed in chunks of 32, with one K tile and one V tile of LDS per
+//    wave.  Both go from HBM straight into LDS (buffer loads with the LDS as
+//    destination), each 1 KB instruction moving whole rows (4 rows at D = 128): K
+//    rows loaded into registers in the MFMA operand layout would touch 16 rows at 64
+//    bytes per instruction, and that gather pattern, not the bytes, was the limit.
+//  * Software pipeline, one stage per chunk t: read K(t)'s operands from LDS, issue
+//    K(t+1) into the K tile, S^T(t) = K Q^T, then the deferred O^T += V^T P^T of
+//    chunk t-1 from the V tile, then issue V(t) into it, then chunk t's softmax.  So
+//    each transfer has about one stage to land, with single-buffered tiles (16 KB of
+//    LDS per wave at D = 128: two workgroups, 8 waves, per compute unit).
 //  * Scores are computed transposed, S^T = K Q^T, so each lane holds ONE head (lane %
 //    16): the online-softmax state (running max in base-2 units, per-lane partial
 //    sum, output rescale) is per-lane work plus a two-step cross-lane max.  Only the
-//    chunk that holds position i is masked.
+//    chunk that holds position i is masked.  The rescale of O by chunk t's max moves
+//    into the accumulator input of chunk t's own P V product in the next stage.
 //  * The exponentials, rounded to bf16, form in accumulator register order the B
 //    operand of O^T += V^T P^T; the V^T operand is read from the row-major LDS tile
 //    with ds_read_b64_tr_b16 (in each 16-lane group, output lane i, value t is
-//    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).  Those reads
-//    sit in one statement with an s_waitcnt vmcnt that awaits exactly this chunk's V
-//    transfer (the next chunk's loads stay in flight); the compiler's own wait for
-//    DMA'd LDS data would be vmcnt(0).
+//    element i % 4 of the 8 bytes that source lane 4t + i/4 addresses).  K and V
+//    operand reads sit in one statement with an s_waitcnt vmcnt that awaits exactly
+//    their own tile's transfer (the younger transfer stays in flight); the compiler's
+//    own wait for DMA'd LDS data would be vmcnt(0).
 //  * Workgroup order keeps each XCD on a contiguous range of (group, query) work so a
 //    group's K/V stays in one XCD's L2.
 #include <type_traits>
@@ -73,6 +79,17 @@ __host__ __device__ constexpr int nsa_swz(int row) {
         return ((row >> 1) & 3) << 1;   // two rows per bank line
 }
 
+// K chunk in LDS: 32 rows x D*2 bytes, row-major, chunk c of row r at slot
+// c ^ nsa_kswz<D>(r): the 16 rows that 16 consecutive lanes read for one MFMA
+// A operand (ds_read_b128, the same 16-byte chunk of each row) cover all 64 banks.
+template <int D>
+__host__ __device__ constexpr int nsa_kswz(int row) {
+    if constexpr (D == 128)
+        return row & 15;                // one row per bank line, 16 chunk slots
+    else
+        return (row >> 1) & 7;          // two rows per bank line, 8 chunk slots
+}
+
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
@@ -87,8 +104,8 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     constexpr int VDMA = VTILE / 1024;       // 1 KB DMA instructions per chunk
     static_assert(BS % kChunk == 0 && VTILE % 1024 == 0, "chunking");
 
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf_a[kWaves][VTILE];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf_b[kWaves][VTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[kWaves][VTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kWaves][VTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -133,14 +150,20 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     }
 
     // ---- per-lane load offsets (bytes within a chunk) ----
-    const int koff = n16 * ROWB + g4 * 16;  // K row 16*kk + n16, dims 32*ds + 8*g4
-    int vdma_off[VDMA];                     // V rows written by DMA instruction j
+    int vdma_off[VDMA], kdma_off[VDMA];     // rows written by DMA instruction j
 #pragma unroll
     for (int j = 0; j < VDMA; ++j) {
         const int pos = j * 1024 + lane * 16;
         const int row = pos / ROWB, slot = (pos % ROWB) >> 4;
         vdma_off[j] = row * ROWB + ((slot ^ nsa_swz<D>(row)) << 4);
+        kdma_off[j] = row * ROWB + ((slot ^ nsa_kswz<D>(row)) << 4);
     }
+    // K operand reads: row n16 (+16 for the upper keys, same swizzle), chunk 4*ds + g4
+    static_assert(nsa_kswz<D>(16) == nsa_kswz<D>(0), "upper keys: same swizzle");
+    uint32_t krd_off[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        krd_off[e] = n16 * ROWB + ((((4 * (e % NDS) + g4)) ^ nsa_kswz<D>(n16)) << 4);
     // V^T operand reads: rows 4*g4 + s/4 (and 16 rows further for the upper keys,
     // same swizzle), dims 16*dt + 4*(s%4)
     const int s16 = n16;
@@ -153,19 +176,13 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
         vrd_off[dt] = row * ROWB + (((col >> 3) ^ nsa_swz<D>(row)) << 4) + (col & 7) * 2;
     }
 
-    typedef uint8_t VTile[kWaves][VTILE];
-    bf16x8 kfa[2][NDS], kfb[2][NDS];  // K operands of the two chunks in flight
-
-    auto load_chunk = [&](int k0, bf16x8 (&kf)[2][NDS], VTile &vt) {
+    auto dma_k = [&](int k0) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int j = 0; j < VDMA; ++j) nsa_dma16(rk, &kbuf[wave][j * 1024], kdma_off[j], k0 * ROWB);
+    };
+    auto dma_v = [&](int k0) {
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds)
-                kf[kk][ds] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                rk, koff + ds * 64, (k0 + 16 * kk) * ROWB, 0));
-#pragma unroll
-        for (int j = 0; j < VDMA; ++j) nsa_dma16(rv, &vt[wave][j * 1024], vdma_off[j], k0 * ROWB);
+        for (int j = 0; j < VDMA; ++j) nsa_dma16(rv, &vbuf[wave][j * 1024], vdma_off[j], k0 * ROWB);
     };
 
     float m = -INFINITY;  // running max of the base-2 scores (this lane's head)
@@ -173,12 +190,74 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     f32x4 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 pprev;              // probabilities of the previous chunk (B operand order)
+    float alpha_prev = 0.0f;   // rescale of O that precedes the previous chunk's P V
 
-    // VM: memory instructions issued after this chunk's V transfer (those of the next
-    // chunk, or none): the V^T reads wait for exactly this chunk's DMA.
-    constexpr int NEXT_OPS = 2 * NDS + VDMA;
-    auto compute_chunk = [&](int k0, const bf16x8 (&kf)[2][NDS], const VTile &vt, auto vm) {
+    // O^T = alpha_prev O^T + V^T P^T of the previous chunk, its V read from the LDS tile
+    // after exactly its own transfer (VM = memory instructions issued after it)
+    auto pv = [&](auto vm) {
         constexpr int VM = decltype(vm)::value;
+        const uint32_t base = lds_addr(&vbuf[wave][0]);
+#pragma unroll
+        for (int d4 = 0; d4 < NDT; d4 += 4) {
+            uint32_t ad[4];
+            bf16x4_t rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + vrd_off[d4 + e];
+            if (d4 == 0)
+                tr_read4x2<VM, 16 * ROWB>(rd, ad);
+            else
+                tr_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x8 a = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3, 4,
+                                                         5, 6, 7);
+                oacc[d4 + e] = mfma_16x16x32(a, pprev, oacc[d4 + e] * alpha_prev);
+            }
+        }
+    };
+    using vdma_ops = std::integral_constant<int, VDMA>;
+    using no_ops = std::integral_constant<int, 0>;
+
+    // Walk the chunks of the kept blocks in slot order: chunk (blk, c) starts at key
+    // blk*BS + 32*c and exists while it starts at or before i.
+    int cur_blk = -1, cur_c = 0;
+    auto next_chunk = [&]() -> int {
+        if (cur_blk >= 0 && cur_c + 1 < NCH && cur_blk * BS + (cur_c + 1) * kChunk <= i) {
+            ++cur_c;
+            return cur_blk * BS + cur_c * kChunk;
+        }
+        if (rem == 0) return -1;
+        const int s = __builtin_ctzll(rem);
+        rem &= rem - 1;
+        cur_blk = __builtin_amdgcn_readlane(myblk, s);
+        cur_c = 0;
+        return cur_blk * BS;
+    };
+
+    // One stage per chunk, with one K tile and one V tile per wave.  Issue order of the
+    // transfers: K(t+1) during stage t, then V(t) once the previous chunk's P V has
+    // read V(t-1); so stage t+1 finds K(t+1) complete when only V(t) is younger, and
+    // the P V of chunk t (in stage t+1) finds V(t) complete when only K(t+2) is.
+    auto stage = [&](int k0, auto first, int &nxt) {
+        constexpr bool kFirst = decltype(first)::value;
+        // K operands: register j of kf[kk] is row 16*kk + n16, dims 32*ds + 8*g4 .. +7
+        bf16x8 kf[2][NDS];
+        {
+            const uint32_t kbase = lds_addr(&kbuf[wave][0]);
+            uint32_t ad[4];
+            u32x4 rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = kbase + krd_off[e];
+            row_read4x2<kFirst ? 0 : VDMA, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                kf[0][ds] = as_bf16x8(rd[2 * ds]);
+                kf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
+            }
+        }
+        nxt = next_chunk();
+        if (nxt >= 0) dma_k(nxt);
         // S^T = K Q^T : register j of st[kk] is key k0 + 16*kk + 4*g4 + j, head n16
         f32x4 st[2];
 #pragma unroll
@@ -187,6 +266,14 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) st[kk] = mfma_16x16x32(kf[kk][ds], qf[ds], st[kk]);
         }
+        // the previous chunk's P V (its V landed while this chunk's K was in flight)
+        if constexpr (!kFirst) {
+            if (nxt >= 0)
+                pv(vdma_ops{});
+            else
+                pv(no_ops{});
+        }
+        dma_v(k0);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) st[kk] *= score_scale;
         if (k0 + kChunk - 1 > i) {  // the chunk holding position i: mask later keys
@@ -205,78 +292,28 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         m = mnew;
         float psum = 0.0f;
-        bf16x8 pf;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float e = __builtin_amdgcn_exp2f(st[kk][j] - mnew);
                 psum += e;
-                pf[kk * 4 + j] = (__bf16)e;
+                pprev[kk * 4 + j] = (__bf16)e;
             }
         lsum = lsum * alpha + psum;
-        // O^T += V^T P^T : register j of oacc[dt] is dim 16*dt + 4*g4 + j, head n16
-        const uint32_t base = lds_addr(&vt[wave][0]);
-#pragma unroll
-        for (int d4 = 0; d4 < NDT; d4 += 4) {
-            uint32_t ad[4];
-            bf16x4_t rd[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ad[e] = base + vrd_off[d4 + e];
-            if (d4 == 0)
-                tr_read4x2<VM, 16 * ROWB>(rd, ad);
-            else
-                tr_read4x2<63, 16 * ROWB>(rd, ad);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x8 a = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3, 4,
-                                                         5, 6, 7);
-                oacc[d4 + e] = mfma_16x16x32(a, pf, oacc[d4 + e] * alpha);
-            }
-        }
-    };
-    using next_loaded = std::integral_constant<int, NEXT_OPS>;
-    using none_loaded = std::integral_constant<int, 0>;
-
-    // Walk the chunks of the kept blocks in slot order: chunk (blk, c) starts at key
-    // blk*BS + 32*c and exists while it starts at or before i.
-    int cur_blk = -1, cur_c = 0;
-    auto next_chunk = [&]() -> int {
-        if (cur_blk >= 0 && cur_c + 1 < NCH && cur_blk * BS + (cur_c + 1) * kChunk <= i) {
-            ++cur_c;
-            return cur_blk * BS + cur_c * kChunk;
-        }
-        if (rem == 0) return -1;
-        const int s = __builtin_ctzll(rem);
-        rem &= rem - 1;
-        cur_blk = __builtin_amdgcn_readlane(myblk, s);
-        cur_c = 0;
-        return cur_blk * BS;
+        alpha_prev = alpha;
     };
 
-    // chunks alternate between (kfa, vbuf_a) and (kfb, vbuf_b); each is fetched one
-    // chunk ahead of its use
-    int ka = next_chunk();
-    if (ka >= 0) load_chunk(ka, kfa, vbuf_a);
-    int kb = ka >= 0 ? next_chunk() : -1;
-    // (a chunk's V^T reads complete before compute_chunk returns, so its tile may be
-    // refilled right after)
-    while (ka >= 0) {
-        if (kb >= 0) {
-            load_chunk(kb, kfb, vbuf_b);
-            compute_chunk(ka, kfa, vbuf_a, next_loaded{});
-        } else {
-            compute_chunk(ka, kfa, vbuf_a, none_loaded{});
-            break;
+    int cur = next_chunk();
+    if (cur >= 0) {
+        dma_k(cur);
+        int nxt;
+        stage(cur, std::true_type{}, nxt);
+        while (nxt >= 0) {
+            cur = nxt;
+            stage(cur, std::false_type{}, nxt);
         }
-        ka = next_chunk();
-        if (ka >= 0) {
-            load_chunk(ka, kfa, vbuf_a);
-            compute_chunk(kb, kfb, vbuf_b, next_loaded{});
-        } else {
-            compute_chunk(kb, kfb, vbuf_b, none_loaded{});
-        }
-        kb = ka >= 0 ? next_chunk() : -1;
+        pv(no_ops{});  // the last chunk's P V: nothing was issued after its V
     }
 
     // finalize: total sum of this head over its 4 lanes
