@@ -17,9 +17,9 @@
 //  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
-//    order, and dQ^T += K^T (.)^T.  V rows go to registers; K goes once into a
-//    per-wave LDS copy of the chunk that serves both the K operand (row reads) and K^T
-//    (transposing reads).  delta is needed before the first dS and is only known after the
+//    order, and dQ^T += K^T (.)^T.  K and V rows go by DMA, whole rows per
+//    instruction, into per-wave LDS tiles of the chunk (double-buffered); the K tile
+//    serves both the K operand (row reads) and K^T (transposing reads).  delta is needed before the first dS and is only known after the
 //    last key, and dout . out from the forward's bf16 output is too coarse a value for
 //    dP - delta, which cancels.  So one pass accumulates, against the estimate
 //    m = dout . out, X = sum_j bf16(P_j (dP_j - m)) k_j, Y = sum_j bf16(P_j) k_j and
@@ -94,6 +94,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
 
     __shared__ __attribute__((aligned(16))) uint8_t kbuf_a[kDqWaves][KTILE];
     __shared__ __attribute__((aligned(16))) uint8_t kbuf_b[kDqWaves][KTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf_a[kDqWaves][KTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf_b[kDqWaves][KTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,8 +149,7 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     }
     const float lse2 = head_ok ? LSE[(size_t)(b * Hq + head) * T + i] * kLog2e : 0.0f;
 
-    const int koff = n16 * ROWB + g4 * 16;  // K or V row 16*kk + n16, dims 32*ds + 8*g4
-    int kdma_off[KDMA];
+    int kdma_off[KDMA];  // K and V tiles alike
 #pragma unroll
     for (int j = 0; j < KDMA; ++j) {
         const int pos = j * 1024 + lane * 16;
@@ -174,16 +175,12 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     for (int ds = 0; ds < NDS; ++ds)
         krow_off[ds] = n16 * ROWB + (((4 * ds + g4) ^ chunk_swz<D>(n16)) << 4);
 
-    // V rows in registers (A operands of dP^T); K only through the LDS copy
-    bf16x8 vfa[2][NDS], vfb[2][NDS];
-    auto load_chunk = [&](int k0, bf16x8 (&vf)[2][NDS], KTileBuf &kt) {  // 2*NDS + KDMA ops
+    // V rows (A operands of dP^T) through an LDS tile of the same layout as K's: each
+    // DMA instruction moves whole rows, where loads in the operand layout would touch
+    // 16 rows at 64 bytes each
+    auto load_chunk = [&](int k0, KTileBuf &vt, KTileBuf &kt) {  // 2*KDMA ops
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds)
-                vf[kk][ds] = __builtin_bit_cast(
-                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, koff + ds * 64,
-                                                                  (k0 + 16 * kk) * ROWB, 0));
+        for (int j = 0; j < KDMA; ++j) bwd_dma16(rv, &vt[wave][j * 1024], kdma_off[j], k0 * ROWB);
 #pragma unroll
         for (int j = 0; j < KDMA; ++j) bwd_dma16(rk, &kt[wave][j * 1024], kdma_off[j], k0 * ROWB);
     };
@@ -223,11 +220,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     float dl = 0.0f;  // this lane's part of delta
     // VM: memory instructions issued after this chunk's K transfer (the next chunk's, or
     // none): the K^T reads wait for exactly this chunk's DMA.
-    constexpr int NEXT_OPS = 2 * NDS + KDMA;
-    auto compute_chunk = [&](int k0, const bf16x8 (&vf)[2][NDS], const KTileBuf &kt, auto vm) {
+    constexpr int NEXT_OPS = 2 * KDMA;
+    auto compute_chunk = [&](int k0, const KTileBuf &vt, const KTileBuf &kt, auto vm) {
         constexpr int VM = decltype(vm)::value;
         const uint32_t base = lds_addr(&kt[wave][0]);
-        bf16x8 kf[2][NDS];
+        bf16x8 kf[2][NDS], vf[2][NDS];
+        {
+            const uint32_t vbase = lds_addr(&vt[wave][0]);
+            uint32_t ad[4];
+            u32x4 rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = vbase + krow_off[e % NDS];
+            row_read4x2<VM, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                vf[0][ds] = as_bf16x8(rd[2 * ds]);
+                vf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
+            }
+        }
         {
             static_assert(NDS == 4 || NDS == 2, "K row reads");
             uint32_t ad[4];
@@ -286,26 +296,26 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         return cur_blk * BS;
     };
 
-    // chunks alternate between (vfa, kbuf_a) and (vfb, kbuf_b), each fetched one chunk
+    // chunks alternate between (vbuf_a, kbuf_a) and (vbuf_b, kbuf_b), each fetched one chunk
     // ahead; a chunk's LDS reads are complete when compute_chunk returns, so its tile
     // may be refilled right after
     int ka = next_chunk();
-    if (ka >= 0) load_chunk(ka, vfa, kbuf_a);
+    if (ka >= 0) load_chunk(ka, vbuf_a, kbuf_a);
     int kb = ka >= 0 ? next_chunk() : -1;
     while (ka >= 0) {
         if (kb >= 0) {
-            load_chunk(kb, vfb, kbuf_b);
-            compute_chunk(ka, vfa, kbuf_a, next_loaded{});
+            load_chunk(kb, vbuf_b, kbuf_b);
+            compute_chunk(ka, vbuf_a, kbuf_a, next_loaded{});
         } else {
-            compute_chunk(ka, vfa, kbuf_a, none_loaded{});
+            compute_chunk(ka, vbuf_a, kbuf_a, none_loaded{});
             break;
         }
         ka = next_chunk();
         if (ka >= 0) {
-            load_chunk(ka, vfa, kbuf_a);
-            compute_chunk(kb, vfb, kbuf_b, next_loaded{});
+            load_chunk(ka, vbuf_a, kbuf_a);
+            compute_chunk(kb, vbuf_b, kbuf_b, next_loaded{});
         } else {
-            compute_chunk(kb, vfb, kbuf_b, none_loaded{});
+            compute_chunk(kb, vbuf_b, kbuf_b, none_loaded{});
         }
         kb = ka >= 0 ? next_chunk() : -1;
     }
