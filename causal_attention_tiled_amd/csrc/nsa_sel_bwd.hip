@@ -18,8 +18,10 @@
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
 //    order, and dQ^T += K^T (.)^T.  K and V rows go by DMA, whole rows per
-//    instruction, into per-wave LDS tiles of the chunk (double-buffered); the K tile
-//    serves both the K operand (row reads) and K^T (transposing reads).  delta is needed before the first dS and is only known after the
+//    instruction, into one K and one V tile of LDS per wave; the K tile serves both
+//    the K operand (row reads) and K^T (transposing reads).  Each chunk's operands
+//    are all read into registers first, so the next chunk's transfers go into the
+//    same tiles right away (16 KB of LDS per wave: 8 waves per compute unit).  delta is needed before the first dS and is only known after the
 //    last key, and dout . out from the forward's bf16 output is too coarse a value for
 //    dP - delta, which cancels.  So one pass accumulates, against the estimate
 //    m = dout . out, X = sum_j bf16(P_j (dP_j - m)) k_j, Y = sum_j bf16(P_j) k_j and
@@ -92,10 +94,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     constexpr int KDMA = KTILE / 1024;
     static_assert(BS % kChunk == 0 && KTILE % 1024 == 0, "chunking");
 
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf_a[kDqWaves][KTILE];
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf_b[kDqWaves][KTILE];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf_a[kDqWaves][KTILE];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf_b[kDqWaves][KTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[kDqWaves][KTILE];
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kDqWaves][KTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -167,7 +167,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         krd_off[dt] = row * ROWB + (((col >> 3) ^ chunk_swz<D>(row)) << 4) + (col & 7) * 2;
     }
 
-    typedef uint8_t KTileBuf[kDqWaves][KTILE];
     // K rows as A operands of S^T, read from the LDS copy: row 16*kk + n16, dims
     // 32*ds + 8*g4 (the kk = 1 rows 16 rows further, same swizzle)
     int krow_off[NDS];
@@ -178,11 +177,11 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     // V rows (A operands of dP^T) through an LDS tile of the same layout as K's: each
     // DMA instruction moves whole rows, where loads in the operand layout would touch
     // 16 rows at 64 bytes each
-    auto load_chunk = [&](int k0, KTileBuf &vt, KTileBuf &kt) {  // 2*KDMA ops
+    auto load_chunk = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < KDMA; ++j) bwd_dma16(rv, &vt[wave][j * 1024], kdma_off[j], k0 * ROWB);
+        for (int j = 0; j < KDMA; ++j) bwd_dma16(rv, &vbuf[wave][j * 1024], kdma_off[j], k0 * ROWB);
 #pragma unroll
-        for (int j = 0; j < KDMA; ++j) bwd_dma16(rk, &kt[wave][j * 1024], kdma_off[j], k0 * ROWB);
+        for (int j = 0; j < KDMA; ++j) bwd_dma16(rk, &kbuf[wave][j * 1024], kdma_off[j], k0 * ROWB);
     };
     // S^T and dP^T of one chunk: register j of st[kk] / dp[kk] is key k0 + 16*kk + 4*g4 + j,
     // head n16; returns the probabilities (0 for keys after i) in pr
@@ -218,70 +217,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
     }
 
     float dl = 0.0f;  // this lane's part of delta
-    // VM: memory instructions issued after this chunk's K transfer (the next chunk's, or
-    // none): the K^T reads wait for exactly this chunk's DMA.
-    constexpr int NEXT_OPS = 2 * KDMA;
-    auto compute_chunk = [&](int k0, const KTileBuf &vt, const KTileBuf &kt, auto vm) {
-        constexpr int VM = decltype(vm)::value;
-        const uint32_t base = lds_addr(&kt[wave][0]);
-        bf16x8 kf[2][NDS], vf[2][NDS];
-        {
-            const uint32_t vbase = lds_addr(&vt[wave][0]);
-            uint32_t ad[4];
-            u32x4 rd[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ad[e] = vbase + krow_off[e % NDS];
-            row_read4x2<VM, 16 * ROWB>(rd, ad);
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) {
-                vf[0][ds] = as_bf16x8(rd[2 * ds]);
-                vf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
-            }
-        }
-        {
-            static_assert(NDS == 4 || NDS == 2, "K row reads");
-            uint32_t ad[4];
-            u32x4 rd[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ad[e] = base + krow_off[e % NDS];
-            row_read4x2<VM, 16 * ROWB>(rd, ad);
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) {
-                kf[0][ds] = as_bf16x8(rd[2 * ds]);
-                kf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
-            }
-        }
-        f32x4 pr[2], dp[2];
-        scores(k0, kf, vf, pr, dp);
-        bf16x8 xf, yf;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                dl = fmaf(pr[kk][j], dp[kk][j], dl);
-                xf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - m));
-                yf[kk * 4 + j] = (__bf16)pr[kk][j];
-            }
-        // X^T += K^T xf^T, Y^T += K^T yf^T (the tile is already in: no vmcnt wait)
-#pragma unroll
-        for (int d4 = 0; d4 < NDT; d4 += 4) {
-            uint32_t ad[4];
-            bf16x4_t rd[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ad[e] = base + krd_off[d4 + e];
-            tr_read4x2<63, 16 * ROWB>(rd, ad);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bf16x8 kt8 = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3,
-                                                           4, 5, 6, 7);
-                xacc[d4 + e] = mfma_16x16x32(kt8, xf, xacc[d4 + e]);
-                yacc[d4 + e] = mfma_16x16x32(kt8, yf, yacc[d4 + e]);
-            }
-        }
-    };
-    using next_loaded = std::integral_constant<int, NEXT_OPS>;
-    using none_loaded = std::integral_constant<int, 0>;
-
     int cur_blk = -1, cur_c = 0;
     auto next_chunk = [&]() -> int {
         if (cur_blk >= 0 && cur_c + 1 < NCH && cur_blk * BS + (cur_c + 1) * kChunk <= i) {
@@ -296,28 +231,81 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         return cur_blk * BS;
     };
 
-    // chunks alternate between (vbuf_a, kbuf_a) and (vbuf_b, kbuf_b), each fetched one chunk
-    // ahead; a chunk's LDS reads are complete when compute_chunk returns, so its tile
-    // may be refilled right after
-    int ka = next_chunk();
-    if (ka >= 0) load_chunk(ka, vbuf_a, kbuf_a);
-    int kb = ka >= 0 ? next_chunk() : -1;
-    while (ka >= 0) {
-        if (kb >= 0) {
-            load_chunk(kb, vbuf_b, kbuf_b);
-            compute_chunk(ka, vbuf_a, kbuf_a, next_loaded{});
-        } else {
-            compute_chunk(ka, vbuf_a, kbuf_a, none_loaded{});
-            break;
+    // One stage per chunk: every operand of the chunk (V and K rows, K^T) is read from
+    // its LDS tiles first -- after all of this wave's transfers, which are then exactly
+    // this chunk's -- and the next chunk's transfers go into the same tiles right after,
+    // with the whole stage to land.
+    auto compute_chunk = [&](int k0, int &nxt) {
+        const uint32_t base = lds_addr(&kbuf[wave][0]);
+        bf16x8 kf[2][NDS], vf[2][NDS], ktf[NDT];
+        {
+            const uint32_t vbase = lds_addr(&vbuf[wave][0]);
+            uint32_t ad[4];
+            u32x4 rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = vbase + krow_off[e % NDS];
+            row_read4x2<0, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                vf[0][ds] = as_bf16x8(rd[2 * ds]);
+                vf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
+            }
         }
-        ka = next_chunk();
-        if (ka >= 0) {
-            load_chunk(ka, vbuf_a, kbuf_a);
-            compute_chunk(kb, vbuf_b, kbuf_b, next_loaded{});
-        } else {
-            compute_chunk(kb, vbuf_b, kbuf_b, none_loaded{});
+        {
+            static_assert(NDS == 4 || NDS == 2, "K row reads");
+            uint32_t ad[4];
+            u32x4 rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + krow_off[e % NDS];
+            row_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                kf[0][ds] = as_bf16x8(rd[2 * ds]);
+                kf[1][ds] = as_bf16x8(rd[2 * ds + 1]);
+            }
         }
-        kb = ka >= 0 ? next_chunk() : -1;
+        // K^T operands of X^T and Y^T: dims 16*dt + 4*g4 .. , keys 4*(n16%4) + .. (both halves)
+#pragma unroll
+        for (int d4 = 0; d4 < NDT; d4 += 4) {
+            uint32_t ad[4];
+            bf16x4_t rd[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ad[e] = base + krd_off[d4 + e];
+            tr_read4x2<63, 16 * ROWB>(rd, ad);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ktf[d4 + e] = __builtin_shufflevector(rd[2 * e], rd[2 * e + 1], 0, 1, 2, 3, 4, 5,
+                                                      6, 7);
+        }
+        nxt = next_chunk();
+        if (nxt >= 0) load_chunk(nxt);
+        f32x4 pr[2], dp[2];
+        scores(k0, kf, vf, pr, dp);
+        bf16x8 xf, yf;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dl = fmaf(pr[kk][j], dp[kk][j], dl);
+                xf[kk * 4 + j] = (__bf16)(pr[kk][j] * (dp[kk][j] - m));
+                yf[kk * 4 + j] = (__bf16)pr[kk][j];
+            }
+        // X^T += K^T xf^T, Y^T += K^T yf^T
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            xacc[dt] = mfma_16x16x32(ktf[dt], xf, xacc[dt]);
+            yacc[dt] = mfma_16x16x32(ktf[dt], yf, yacc[dt]);
+        }
+    };
+
+    int cur = next_chunk();
+    if (cur >= 0) {
+        load_chunk(cur);
+        while (cur >= 0) {
+            int nxt;
+            compute_chunk(cur, nxt);
+            cur = nxt;
+        }
     }
 
     dl += __shfl_xor(dl, 16);
