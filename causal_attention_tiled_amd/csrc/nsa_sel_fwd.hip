@@ -100,8 +100,8 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     constexpr int NCH = BS / kChunk;         // chunks per selected block
     constexpr int NDS = D / 32;              // S^T MFMA k-steps
     constexpr int NDT = D / 16;              // 16-dim output tiles
-    constexpr int VTILE = kChunk * ROWB;     // bytes of one V chunk
-    constexpr int VDMA = VTILE / 1024;       // 1 KB DMA instructions per chunk
+    constexpr int VTILE = kChunk * ROWB;     // bytes of one K (or V) chunk
+    constexpr int VDMA = VTILE / 1024;       // 1 KB DMA instructions per chunk and tensor
     static_assert(BS % kChunk == 0 && VTILE % 1024 == 0, "chunking");
 
     __shared__ __attribute__((aligned(16))) uint8_t kbuf[kWaves][VTILE];
@@ -159,6 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
         kdma_off[j] = row * ROWB + ((slot ^ nsa_kswz<D>(row)) << 4);
     }
     // K operand reads: row n16 (+16 for the upper keys, same swizzle), chunk 4*ds + g4
+    // (at D = 64, NDS = 2: the last two addresses repeat the first two, reads unused)
     static_assert(nsa_kswz<D>(16) == nsa_kswz<D>(0), "upper keys: same swizzle");
     uint32_t krd_off[4];
 #pragma unroll
@@ -190,7 +191,8 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     f32x4 oacc[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    bf16x8 pprev;              // probabilities of the previous chunk (B operand order)
+    bf16x8 pprev;              // probabilities of the previous chunk (B operand order;
+                               // set by every stage before the P V that reads it)
     float alpha_prev = 0.0f;   // rescale of O that precedes the previous chunk's P V
 
     // O^T = alpha_prev O^T + V^T P^T of the previous chunk, its V read from the LDS tile
