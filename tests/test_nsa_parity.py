@@ -32,6 +32,8 @@ SMALL = [  # B, Hq, Hkv, T, D, bs, S
     (1, 3, 1, 64, 64, 64, 1),       # one block, S = 1
     (2, 10, 2, 320, 64, 32, 16),    # G = 5, many slots
     (1, 4, 2, 2048, 64, 32, 64),    # S = 64, the most slots (one per lane): every block
+    (1, 4, 2, 96, 128, 32, 2),      # D = 128 with 32-key blocks: one chunk per block
+    (2, 8, 1, 384, 128, 64, 1),     # S = 1: only the own block (one or two chunks per query)
 ]
 
 
