@@ -81,6 +81,25 @@ def nsa_gathered_bytes(idx, T, bs, D, rows_kv=None):
     return float(distinct.sum()) * 2 * bs * D * 2
 
 
+def nsa_useful_flops(idx, T, bs, D, G):
+    """4*D FLOPs (q.k and p*v) per (query head, attended token): the attended tokens of
+    query i are those j <= i of its distinct, in-range selected blocks."""
+    nblk = T // bs
+    flat = idx.reshape(-1, idx.shape[-1])
+    pos = (np.arange(flat.shape[0]) % T)[:, None]
+    srt = np.sort(flat, axis=1)
+    first = np.concatenate([np.ones((srt.shape[0], 1), bool), srt[:, 1:] != srt[:, :-1]], axis=1)
+    ok = first & (srt >= 0) & (srt < nblk) & (srt * bs <= pos)
+    tokens = np.where(ok, np.minimum(bs, pos - srt * bs + 1), 0).sum()
+    return 4.0 * D * G * float(tokens)
+
+
+def nsa_unique_bytes(B, Hq, Hkv, T, D, S):
+    """Bytes every nsa_sel_fwd launch must move at least once: q, k, v, block_idx read,
+    out and lse written."""
+    return float(2 * B * Hkv * T * D * 2 + 2 * B * Hq * T * D * 2 + B * Hq * T * 4 + B * Hkv * T * S * 4)
+
+
 def kernel_source_hash(name):
     """Hash of the kernel's sources and the build script; in the C/HIP files, // comments
     and blank lines are left out, so an edit of a comment keeps a measurement valid and
@@ -310,6 +329,26 @@ def extra_configs(dev, nsa_c5=None):
     return res
 
 
+def measured_ceilings():
+    """Ceilings measured on this GPU by the probes in libprobes.so: streaming read
+    bandwidth of a buffer served by L2 (16 MiB), by the memory-side cache (128 MiB) and
+    by HBM (4 GiB); bf16 MFMA TFLOP/s with the engine clock seen during it; v_log_f32 +
+    v_exp_f32 lane operations per second."""
+    from causal_attention_tiled_amd import probes
+    res = {}
+    for name, nbytes in (("read_l2_gbps", 16 << 20), ("read_mall_gbps", 128 << 20),
+                         ("read_hbm_gbps", 4 << 30)):
+        res[name] = probes.read_bandwidth(nbytes)
+    res["mfma_bf16_tflops"], res["sclk_ghz_under_mfma"] = probes.mfma_rate()
+    res["log_exp_lane_ops_per_s"] = probes.transcendental_rate()
+    res["note"] = ("read: 16-byte loads by 2048 workgroups of 256 threads, each re-reading "
+                   "its own elements, of 16 MiB (L2-resident), 128 MiB (MALL-resident) and "
+                   "4 GiB (HBM); mfma: 4 chains of v_mfma_f32_32x32x16_bf16 per wave, 8 waves "
+                   "per CU, clock = shader cycles (s_memtime) over 100 MHz ticks "
+                   "(s_memrealtime); log/exp: 8 chains of v_log_f32, v_exp_f32 per lane")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -323,6 +362,8 @@ def main():
                          "reference for calibrating HBM traffic counters")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the timings of the other configurations")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the probe measurements of read, MFMA and log/exp ceilings")
     ap.add_argument("--source-hashes", action="store_true",
                     help="print the source hash of each kernel and exit")
     args = ap.parse_args()
@@ -406,11 +447,39 @@ def main():
                 "achieved": tra_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": tra_tflops / PEAK_BF16_TFLOPS, "traffic": recorded_traffic("tra_fwd"),
                 "per_launch": f"{flops:.6g} useful FLOPs / {tra_avg:.4f} ms avg launch"}
-    roof_nsa = {"kernel": "nsa_sel_fwd_kernel<128,64>", "bound": "hbm",
-                "achieved": nsa_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": nsa_gbps / PEAK_HBM_GBPS, "traffic": recorded_traffic("nsa_sel_fwd"),
-                "per_launch": f"{gbytes:.6g} gathered K/V bytes / {nsa_avg:.4f} ms avg launch"}
+    # NSA roofline: the larger of the time its useful FLOPs need at the bf16 MFMA peak and
+    # the time its unique bytes need at the HBM peak (the gathered K/V is mostly served
+    # from L2 and the memory-side cache, so gathered bytes over HBM bandwidth is no bound)
+    G = NSA["Hq"] // NSA["Hkv"]
+    nsa_flops = nsa_useful_flops(idx_np, NSA["T"], NSA["block_size"], NSA["D"], G)
+    nsa_ubytes = nsa_unique_bytes(NSA["B"], NSA["Hq"], NSA["Hkv"], NSA["T"], NSA["D"], NSA["S"])
+    t_flop_ms = nsa_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+    t_byte_ms = nsa_ubytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+    nsa_tflops = nsa_flops / (nsa_avg * 1e-3) / 1e12 if run_nsa else 0.0
+    if t_flop_ms >= t_byte_ms:
+        roof_nsa = {"kernel": "nsa_sel_fwd_kernel<128,64>", "bound": "mfma",
+                    "achieved": nsa_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": nsa_tflops / PEAK_BF16_TFLOPS if run_nsa else 0.0}
+    else:
+        ubps = nsa_ubytes / (nsa_avg * 1e-3) / 1e9 if run_nsa else 0.0
+        roof_nsa = {"kernel": "nsa_sel_fwd_kernel<128,64>", "bound": "hbm",
+                    "achieved": ubps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": ubps / PEAK_HBM_GBPS}
+    roof_nsa.update({
+        "traffic": recorded_traffic("nsa_sel_fwd"),
+        "per_launch": f"{nsa_flops:.6g} useful FLOPs ({t_flop_ms:.4f} ms at peak) and "
+                      f"{nsa_ubytes:.6g} unique bytes ({t_byte_ms:.4f} ms at peak) / "
+                      f"{nsa_avg:.4f} ms avg launch",
+        "gathered_gbps": nsa_gbps,
+        "gathered_note": f"{gbytes:.6g} gathered K/V bytes per launch (each selected block's "
+                         "K and V once per GQA group) over the launch time; mostly served from "
+                         "L2 and the memory-side cache, so not a fraction of HBM bandwidth"})
     dominant = roof_nsa if nsa_avg >= tra_avg else roof_tra
+    ceilings = measured_ceilings() if not args.no_ceilings else None
+    if ceilings is not None and roof_nsa.get("traffic") and run_nsa:
+        rate = roof_nsa["traffic"] / (nsa_avg * 1e-3) / 1e9
+        roof_nsa["l2_miss_gbps"] = rate
+        roof_nsa["l2_miss_frac_of_mall_read_ceiling"] = rate / ceilings["read_mall_gbps"]
 
     result = {
         "metric": METRIC,
@@ -434,10 +503,16 @@ def main():
                     "frac_bf16_peak": tra_tflops / PEAK_BF16_TFLOPS},
         "nsa_sel_fwd": {"ms": nsa_avg, "ms_median": float(np.median(nsa_ms)),
                         "ms_min": float(np.min(nsa_ms)), "gathered_gb": gbytes / 1e9,
-                        "gbps": nsa_gbps, "frac_hbm_peak": nsa_gbps / PEAK_HBM_GBPS},
+                        "gathered_gbps": nsa_gbps,
+                        "gathered_over_hbm_peak": nsa_gbps / PEAK_HBM_GBPS,
+                        "useful_tflops": nsa_tflops,
+                        "frac_bf16_peak": nsa_tflops / PEAK_BF16_TFLOPS,
+                        "unique_gb": nsa_ubytes / 1e9},
         "roofline": dominant,
         "roofline_all": {"tra_fwd": roof_tra, "nsa_sel_fwd": roof_nsa},
     }
+    if ceilings is not None:
+        result["ceilings"] = ceilings
     if not args.no_extra and args.only is None:
         print("bench: other configurations", file=sys.stderr, flush=True)
         c5 = (lambda: cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n),

@@ -3,8 +3,9 @@
     python -m causal_attention_tiled_amd.build [--asm]
 
 Each csrc/*.hip file is compiled to an object under _build/, then linked into
-causal_attention_tiled_amd/libattn.so.  ``--asm`` also keeps the gfx950
-assembly of each object under _build/ for inspection.
+causal_attention_tiled_amd/libattn.so.  The measurement probes (probes/probes.hip)
+are linked on their own into causal_attention_tiled_amd/probes/libprobes.so.
+``--asm`` also keeps the gfx950 assembly of each object under _build/ for inspection.
 """
 from __future__ import annotations
 
@@ -19,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+PROBES_SRC = os.path.join(PKG, "probes", "probes.hip")
+PROBES_LIB = os.path.join(PKG, "probes", "libprobes.so")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -67,6 +70,12 @@ def build(asm: bool = False, verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = PROBES_LIB + ".tmp"
+    cmd = [hipcc, *CXXFLAGS, "-shared", PROBES_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=BUILD)
+    os.replace(tmp, PROBES_LIB)
     return LIB
 
 

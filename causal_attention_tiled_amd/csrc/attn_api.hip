@@ -18,6 +18,11 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
 // The grid is one dimension of at most 2^31-1 workgroups.
 bool grid_fits(int64_t n) { return n > 0 && n <= 0x7fffffffLL; }
 
+// The bf16 kernels read a (batch, head) slab of T x D elements through a buffer
+// resource with 32-bit byte offsets (rows past the slab read as zero), so a slab
+// must stay below 2^31 bytes.
+bool bf16_slab_fits(int T, int D) { return (int64_t)T * D * 2 < ((int64_t)1 << 31); }
+
 int tra_validate(const void *q, const void *k, const void *v, const void *out, int B, int H,
                  int T, int D, float beta, float p, int rows_per_wg, bool *noop) {
     *noop = false;
@@ -55,6 +60,7 @@ int nsa_validate(const void *q, const void *k, const void *v, const int32_t *blo
     if (misaligned(q) || misaligned(k) || misaligned(v)) return ATTN_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(block_idx) & 3u) != 0) return ATTN_ERR_ALIGN;
     if (!grid_fits((int64_t)B * Hkv * ((T + 3) / 4))) return ATTN_ERR_SHAPE;
+    if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     return ATTN_OK;
 }
 
@@ -72,6 +78,7 @@ ATTN_EXPORT int tra_fwd(const void *q, const void *k, const void *v, void *out, 
     bool noop;
     const int st = tra_validate(q, k, v, out, B, H, T, D, beta, p, attn::tra_bf16_rows(D), &noop);
     if (st != ATTN_OK || noop) return st;
+    if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     const hipError_t e = attn::launch_tra_fwd_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), static_cast<uint16_t *>(out), B * H, T, D, beta, p,
@@ -95,6 +102,7 @@ ATTN_EXPORT int tra_bwd(const void *q, const void *k, const void *v, const void 
     bool noop;
     const int st = tra_validate(q, k, v, dq, B, H, T, D, beta, p, attn::kTraBwdDkvRows, &noop);
     if (st != ATTN_OK || noop) return st;
+    if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     if (!dout || !dk || !dv) return ATTN_ERR_NULL;
     if (misaligned(dout) || misaligned(dk) || misaligned(dv)) return ATTN_ERR_ALIGN;
     const hipError_t e = attn::launch_tra_bwd_bf16(
@@ -118,6 +126,7 @@ ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const vo
     bool noop;
     const int st = tra_validate(q1, k1, v, out, B, H, T, D, beta, p, attn::kTdaRows, &noop);
     if (st != ATTN_OK || noop) return st;
+    if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     if (!q2 || !k2) return ATTN_ERR_NULL;
     if (misaligned(q2) || misaligned(k2)) return ATTN_ERR_ALIGN;
     const size_t need = tda_workspace_bytes(B, H, T, D, normalize);

@@ -18,9 +18,11 @@
 // K1, K2 and V staged HBM -> LDS by buffer loads, double-buffered, V read
 // transposed from LDS.
 //
-// Normalisation: a query row is normalised in registers when the wave loads it.
-// Key rows are normalised once, by a row-normalisation pass that writes them to
-// the caller's workspace, since every workgroup of a head re-reads the keys.
+// Normalisation, as torch.nn.functional.normalize does on the page's bf16 tensors:
+// the row's 2-norm rounded to bf16 (at least 1e-12), then each element divided by
+// it and rounded to bf16.  A query row is normalised in registers when the wave
+// loads it.  Key rows are normalised once, by a row-normalisation pass that writes
+// them to the caller's workspace, since every workgroup of a head re-reads the keys.
 #include <type_traits>
 
 #include "attn_tile.h"
@@ -32,9 +34,28 @@ constexpr int kWaves = 8;  // wavefronts per workgroup, 32 query rows each
 static_assert(kWaves * 32 == kTdaRows, "workgroup rows");
 constexpr int kBN = 64;    // keys per LDS tile
 
-// Row L2 normalisation, bf16 -> bf16: y = x / max(||x||_2, 1e-12), the sum of
-// squares in fp32.  D/8 lanes per row, 16 bytes per lane; blockIdx.y picks one of
-// two tensors.
+// torch.nn.functional.normalize on a bf16 tensor divides by a bf16 norm, clamped
+// below at 1e-12 (also a bf16 value: 0x2b8d as bf16 bits).
+constexpr float kNormEps = 1.0018652574217413e-12f;
+
+// The bf16 value nearest (ties to even) to sqrt(ss), as a float.  ss is the sum of
+// squares of a bf16 row accumulated in fp64, which is exact unless the row's
+// magnitudes span about 2^30; the fp64 square root is then rounded straight to 8
+// significant bits (no intermediate fp32 rounding), so the result is the exact
+// norm rounded once, except where that lies within ~2^-50 of a bf16 midpoint.
+__device__ __forceinline__ float bf16_norm(double ss) {
+    uint64_t b = __builtin_bit_cast(uint64_t, __builtin_sqrt(ss));
+    b += (((uint64_t)1 << 44) - 1) + ((b >> 45) & 1);  // nearest-even at bit 45
+    b &= ~(((uint64_t)1 << 45) - 1);
+    return fmaxf((float)__builtin_bit_cast(double, b), kNormEps);
+}
+// Each normalised element is bf16(x / n) for bf16 values x and n.  Such a quotient
+// is never within 2^-17 (relative) of a bf16 rounding midpoint, so x * (1/n) in
+// fp32 (relative error below 2^-22) rounds to the same bf16 value as the exact
+// quotient does.
+
+// Row L2 normalisation, bf16 -> bf16: y = bf16(x / bf16_norm(sum x^2)).  D/8 lanes
+// per row, 16 bytes per lane; blockIdx.y picks one of two tensors.
 template <int D>
 __global__ __launch_bounds__(256) void l2norm_rows_kernel(const uint16_t *__restrict__ x0,
                                                           const uint16_t *__restrict__ x1,
@@ -52,15 +73,16 @@ __global__ __launch_bounds__(256) void l2norm_rows_kernel(const uint16_t *__rest
     if (row >= rows) return;
     const u32x4 raw = *(const u32x4 *)(x + row * D + part * 8);
     const bf16x8 e = as_bf16x8(raw);
-    float f[8], ss = 0.0f;
+    float f[8];
+    double ss = 0.0;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         f[t] = (float)e[t];
-        ss = fmaf(f[t], f[t], ss);
+        ss = __builtin_fma((double)f[t], (double)f[t], ss);
     }
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
-    const float r = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    const float r = 1.0f / bf16_norm(ss);
     const u32x4 o = {pack_bf16x2(f[0] * r, f[1] * r), pack_bf16x2(f[2] * r, f[3] * r),
                      pack_bf16x2(f[4] * r, f[5] * r), pack_bf16x2(f[6] * r, f[7] * r)};
     *(u32x4 *)(y + row * D + part * 8) = o;
@@ -174,13 +196,16 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
     }
     if (norm_q) {
         auto qnorm = [&](bf16x8 (&qf)[NDS]) {
-            float ss = 0.0f;
+            double ss = 0.0;
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-                for (int t = 0; t < 8; ++t) ss = fmaf((float)qf[ds][t], (float)qf[ds][t], ss);
+                for (int t = 0; t < 8; ++t) {
+                    const double x = (double)(float)qf[ds][t];
+                    ss = __builtin_fma(x, x, ss);
+                }
             ss += __shfl_xor(ss, 32, 64);
-            const float r = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+            const float r = 1.0f / bf16_norm(ss);
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll

@@ -1,0 +1,127 @@
+// probes.hip -- microbenchmarks that measure ceilings of the MI355X for the rooflines
+// reported next to the attention kernels (built into libprobes.so, not into
+// libattn.so; bench.py and the profiling runs load it):
+//  * read_kernel: streaming 16-byte loads over a buffer, each workgroup always reading
+//    the same elements, so that a buffer sized under the L2 of the reading XCD (4 MiB
+//    each) is served by L2, one sized between the L2s and the memory-side cache (MALL,
+//    256 MiB) by the MALL, and a larger one by HBM;
+//  * mfma_kernel: independent chains of v_mfma_f32_32x32x16_bf16, timed by the shader
+//    clock counter (s_memtime) and the constant 100 MHz counter (s_memrealtime) on
+//    each wave, whose ratio is the engine clock under MFMA load;
+//  * trans_kernel: independent chains of v_log_f32 followed by v_exp_f32 (the pair the
+//    general-power epilogue x^p = exp2(p log2 x) issues per element).
+// Every loop is bounded by its arguments and every access stays inside its buffer.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define PROBE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kNever = 0x9e3779b9u;  // a value the reductions below practically never take
+
+// n elements of 16 bytes; thread (workgroup w, lane t) reads elements w*256 + t + k*stride
+// in every pass, four loads in flight per thread.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ buf, int64_t n,
+                                                   int passes, uint32_t *__restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (int p = 0; p < passes; ++p) {
+        int64_t i = first;
+        for (; i + 3 * stride < n; i += 4 * stride) {
+            const u32x4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride],
+                        d = buf[i + 3 * stride];
+            const u32x4 x = a ^ b ^ c ^ d;
+            acc ^= x.x ^ x.y ^ x.z ^ x.w;
+        }
+        for (; i < n; i += stride) {
+            const u32x4 a = buf[i];
+            acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        }
+    }
+    if (acc == kNever) sink[0] = acc;
+}
+
+// Four independent accumulators per wave; clk[2*w] = shader clock cycles and
+// clk[2*w + 1] = 100 MHz ticks spent by wave w in the loop.
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float *__restrict__ sink,
+                                                   uint64_t *__restrict__ clk) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        a[t] = (__bf16)(0.001f * (float)(lane + t));
+        b[t] = (__bf16)(0.002f * (float)(lane - t));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (s == 1234.5f) sink[0] = s;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (lane == 0) {
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = r1 - r0;
+    }
+}
+
+// Eight independent chains per lane of x <- 2^-|log2 |x||, which stays in (0, 1]:
+// each step is one v_log_f32 and one v_exp_f32 with input modifiers only.
+__global__ __launch_bounds__(256) void trans_kernel(int iters, float *__restrict__ sink) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.3f + 0.01f * (float)((threadIdx.x + j) & 31);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            x[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(__builtin_amdgcn_logf(__builtin_fabsf(x[j]))));
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += x[j];
+    if (s == 1234.5f) sink[0] = s;
+}
+
+}  // namespace
+
+// Streaming read of `bytes` (a multiple of 16) at `buf`, `passes` times, by `grid`
+// workgroups of 256 threads.  Returns the HIP launch status.
+PROBE_EXPORT int probe_read(const void *buf, int64_t bytes, int passes, int grid, void *sink,
+                            void *stream) {
+    if (!buf || !sink || bytes < 16 || (bytes & 15) || passes < 1 || grid < 1) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)buf, bytes / 16, passes, (uint32_t *)sink);
+    return (int)hipGetLastError();
+}
+
+// `iters` iterations of 4 MFMAs (32x32x16 bf16, 32768 FLOPs each) per wave, `grid`
+// workgroups of 4 waves; clk holds 2 uint64 per wave (shader cycles, 100 MHz ticks).
+PROBE_EXPORT int probe_mfma(int iters, int grid, void *sink, void *clk, void *stream) {
+    if (!sink || !clk || iters < 1 || grid < 1) return -1;
+    hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
+                       (float *)sink, (uint64_t *)clk);
+    return (int)hipGetLastError();
+}
+
+// `iters` iterations of 8 (log, exp) pairs per lane, `grid` workgroups of 256 threads.
+PROBE_EXPORT int probe_trans(int iters, int grid, void *sink, void *stream) {
+    if (!sink || iters < 1 || grid < 1) return -1;
+    hipLaunchKernelGGL(trans_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
+                       (float *)sink);
+    return (int)hipGetLastError();
+}

@@ -13,8 +13,11 @@
  *    enqueued asynchronously; no call synchronises the device or the host.
  *  - Output buffers are fully overwritten (every element is written).
  *  - All arguments are validated on the host before any HIP call.  On a
- *    validation error nothing is enqueued.  Element offsets are computed in
- *    64-bit, so tensors may exceed 2^31 elements.
+ *    validation error nothing is enqueued.  Offsets between (batch, head)
+ *    slabs are computed in 64-bit, so tensors may exceed 2^31 elements; the
+ *    bf16 kernels address within one slab of T x D elements with 32-bit byte
+ *    offsets, so every bf16 entry point requires T * D * 2 < 2^31 (T < 2^23
+ *    at D = 128, T < 2^24 at D = 64), else ATTN_ERR_UNSUPPORTED.
  *  - The library is stateless and may be called from several host threads.
  *  - A size of zero in B, H/Hq or T is a successful no-op once the other
  *    arguments have been validated; the tensor pointers may then be NULL.
@@ -130,6 +133,10 @@ int tra_bwd(const void *q, const void *k, const void *v, const void *dout,
  *   beta, lambda      : finite (else ATTN_ERR_SHAPE)
  *   p                 : finite and > 0 (else ATTN_ERR_SHAPE)
  *
+ * Normalisation follows torch.nn.functional.normalize on bf16 tensors: the
+ * row's 2-norm is itself rounded to bf16 (nearest-even, at least the bf16 value
+ * of 1e-12) and each element x / norm is rounded to bf16.
+ *
  * Numerics: as tra_fwd; normalised rows are rounded to bf16; the two
  * weights of a pair are combined in fp32 and rounded to bf16 once, and one
  * fp32 accumulation over v gives the output (rounded to bf16 once).
@@ -171,7 +178,8 @@ size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize);
  *   block_size : 32, 64 or 128                 (else ATTN_ERR_UNSUPPORTED)
  *   Hq % Hkv   : must be 0                     (else ATTN_ERR_SHAPE)
  *   G = Hq/Hkv : 1 .. 16                       (else ATTN_ERR_UNSUPPORTED)
- *   T          : a multiple of block_size      (else ATTN_ERR_SHAPE)
+ *   T          : a multiple of block_size      (else ATTN_ERR_SHAPE), and
+ *                T * D * 2 < 2^31               (else ATTN_ERR_UNSUPPORTED)
  *   S          : 1 .. 64                       (< 1: ATTN_ERR_SHAPE, > 64: ATTN_ERR_UNSUPPORTED)
  *
  * Numerics: scores in fp32 from bf16 products; softmax state (running max,

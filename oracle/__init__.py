@@ -23,6 +23,10 @@ Functions
     rows, two Threshold Rectified Attention outputs over the same v, combined
     as out1 - clamp(lam, 0, 1) * out2.  Source: snap-research/TDA page
     "triton_threshold_attention.py", ``differential_threshold_rela_triton``.
+``l2norm_ref(x)``
+    The row normalisation of ``tda_ref``: x / max(||x||_2, 1e-12) with the norm rounded
+    to the input dtype before the divide, as ``torch.nn.functional.normalize`` gives on
+    a tensor of that dtype.
 ``nsa_ref(q, k, v, block_idx, block_size, rows=None)``
     NSA selection-branch forward (GQA softmax over the union of the selected
     blocks' causal tokens, scale D^-0.5), returning (out, lse).  Source:
@@ -88,6 +92,8 @@ def _load():
                                         i64, i64, i64, vp, i64, vp, vp, i64, vp, vp,
                                         ctypes.c_int]
     lib.oracle_nsa_bwd_rows.restype = ctypes.c_int
+    lib.oracle_l2norm_rows.argtypes = [vp, ctypes.c_int, i64, i64, vp]
+    lib.oracle_l2norm_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -246,6 +252,21 @@ def tda_ref(q1, q2, k1, k2, v, beta: float, lam: float, p: float, normalize: boo
     if rc != 0:
         raise ValueError("oracle_tda_rows rejected its arguments")
     return out.reshape(B, H, T, D) if r is None else out
+
+
+def l2norm_ref(x) -> np.ndarray:
+    """The row normalisation that ``tda_ref(..., normalize=True)`` applies to q1, q2, k1
+    and k2: each row over the last axis divided by its 2-norm rounded to the input dtype
+    (at least 1e-12), each quotient rounded to the dtype.  Source: the page's
+    ``differential_threshold_rela_triton`` normalises tensors of the input dtype with
+    ``torch.nn.functional.normalize``.  Returns float64 of x's shape."""
+    xa, dt = _as_input(x)
+    D = xa.shape[-1]
+    n = xa.size // D
+    out = np.zeros((n, D), dtype=np.float64)
+    if _load().oracle_l2norm_rows(xa.ctypes.data, dt, n, D, out.ctypes.data) != 0:
+        raise ValueError("oracle_l2norm_rows rejected its arguments")
+    return out.reshape(xa.shape)
 
 
 def nsa_ref(q, k, v, block_idx, block_size: int, rows=None, nthreads: int = 0):

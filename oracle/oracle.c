@@ -248,11 +248,13 @@ static double round_to_dtype(double x, int dtype) {
     return ldexp(r, e - 8);
 }
 
-/* Row `row` (D values) of a [.., D] array, widened; with `normalize` divided by
- * max(||row||_2, 1e-12) as torch.nn.functional.normalize(p=2, dim=-1) does, and
- * the quotient rounded back to the input dtype: the page normalises tensors of
- * the input dtype and hands the normalised tensors, in that dtype, to the
- * attention. */
+/* Row `row` (D values) of a [.., D] array, widened; with `normalize` it is
+ * normalised as torch.nn.functional.normalize(p=2, dim=-1) does on a tensor of
+ * the input dtype: the norm is itself a value of that dtype (the exact 2-norm,
+ * rounded once to nearest-even), clamped below at 1e-12 (as a value of that
+ * dtype), and each quotient x / norm is rounded to the dtype.  The page
+ * normalises tensors of the input dtype and hands the normalised tensors, in
+ * that dtype, to the attention. */
 static void load_row(const void *x, int dtype, int64_t row, int64_t D, int normalize,
                      double *dst) {
     double ss = 0.0;
@@ -261,9 +263,23 @@ static void load_row(const void *x, int dtype, int64_t row, int64_t D, int norma
         ss += dst[d] * dst[d];
     }
     if (!normalize) return;
-    double nrm = sqrt(ss);
-    if (nrm < 1e-12) nrm = 1e-12;
+    double nrm = round_to_dtype(sqrt(ss), dtype);
+    const double eps = round_to_dtype(1e-12, dtype);
+    if (nrm < eps) nrm = eps;
     for (int64_t d = 0; d < D; ++d) dst[d] = round_to_dtype(dst[d] / nrm, dtype);
+}
+
+/*
+ * The normalised rows that the Threshold Differential Attention forward below
+ * works on (normalize != 0): rows [nrows, D] of fp32 or bf16 bits in, doubles
+ * out (each a value of the input dtype).  Exposed so that tests can compare the
+ * normalisation on its own with torch's.  Returns 0, or -1 on bad arguments.
+ */
+int oracle_l2norm_rows(const void *x, int dtype, int64_t nrows, int64_t D, double *out) {
+    if (!x || !out || nrows < 0 || D <= 0) return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    for (int64_t r = 0; r < nrows; ++r) load_row(x, dtype, r, D, 1, out + r * D);
+    return 0;
 }
 
 /*
@@ -273,9 +289,10 @@ static void load_row(const void *x, int dtype, int64_t row, int64_t D, int norma
  *   rows              : flat row ids r = (b*H + h)*T + i, or NULL for all rows
  *   out               : [nrows, D] doubles
  *
- * With normalize != 0 every row of q1, q2, k1, k2 is first divided by
- * max(||row||_2, 1e-12) and rounded back to the input dtype (bf16 or fp32,
- * nearest-even), as the page's normalised tensors are.  Then, the two paths
+ * With normalize != 0 every row of q1, q2, k1, k2 is first normalised as
+ * load_row states: divided by its 2-norm rounded to the input dtype (at least
+ * 1e-12), each quotient rounded to the dtype (bf16 or fp32, nearest-even), as
+ * the page's normalised tensors are.  Then, the two paths
  * taken one after the other as the page does,
  *
  *   out1 = sum_{j<=i} max(q1_i . k1_j - tau_i, 0)^p v_j

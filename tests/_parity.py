@@ -4,9 +4,10 @@ Tolerance for an output row (the D values of one (b, h, i)):
     |gpu - ref| <= rel * max_d |ref row| + rel * |ref|      elementwise,
 with rel = 1e-2 for bf16 outputs and 1e-4 for fp32 outputs.  A reference row
 that is all zero therefore demands an exact zero, unless the caller adds a floor
-``floor * max |ref|`` taken over the whole compared tensor (used where the exact
-result is zero only by cancellation of terms the kernel rounds, e.g. a softmax
-gradient over a single attended key).  lse:
+``floor * max |ref|`` (taken over the whole compared tensor) on the rows that
+``floor_rows`` marks: rows whose exact result is zero only by cancellation of
+terms the kernel rounds (the softmax gradient of a query that attends a single
+key).  lse:
     |gpu - ref| <= 1e-3 * (1 + |ref|), and the empty-row sentinel -1e9 exactly.
 """
 import numpy as np
@@ -23,14 +24,20 @@ def to_np(t):
     return np.asarray(t, dtype=np.float64)
 
 
-def assert_rows_close(gpu, ref, rel, what="", floor=0.0):
+def assert_rows_close(gpu, ref, rel, what="", floor=0.0, floor_rows=None):
+    """Elementwise row tolerance; with ``floor`` and ``floor_rows`` (a boolean mask over
+    the leading dimensions, i.e. one flag per output row) the flagged rows get the extra
+    absolute allowance floor * max|ref|."""
     g = to_np(gpu)
     r = np.asarray(ref, dtype=np.float64)
     assert g.shape == r.shape, (g.shape, r.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output"
     bound = rel * np.abs(r).max(axis=-1, keepdims=True) + rel * np.abs(r)
     if floor and r.size:
-        bound = bound + floor * np.abs(r).max()
+        assert floor_rows is not None, "a floor needs the rows it applies to"
+        fr = np.asarray(floor_rows, dtype=bool)
+        assert fr.shape == r.shape[:-1], (fr.shape, r.shape)
+        bound = bound + np.where(fr[..., None], floor * np.abs(r).max(), 0.0)
     err = np.abs(g - r)
     bad = err > bound
     if bad.any():

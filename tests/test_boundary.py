@@ -208,3 +208,15 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
             src = open(os.path.join(pkg, name)).read()
             assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), name
             assert "liboracle" not in src, name
+
+
+@pytest.mark.parametrize("D,T", [(128, 1 << 23), (64, 1 << 24), (128, (1 << 23) + 64)])
+def test_bf16_slab_byte_limit(lib, D, T):
+    """The bf16 kernels address one (batch, head) slab of T x D elements with 32-bit
+    byte offsets: T * D * 2 >= 2^31 is refused before any HIP call."""
+    assert _tra(lib, "tra_fwd", T=T, D=D) == EUNSUP
+    assert _bwd(lib, T=T, D=D) == EUNSUP
+    assert _tda(lib, T=T, D=D) == EUNSUP
+    assert _nsa(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP
+    assert _nbwd(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP
+    assert _fsa(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP

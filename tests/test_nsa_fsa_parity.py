@@ -13,7 +13,7 @@ import oracle
 import causal_attention_tiled_amd as cat
 from causal_attention_tiled_amd import inputs
 
-from _parity import BF16_REL, assert_lse_close, assert_rows_close, sample_rows
+from _parity import BF16_REL, assert_lse_close, assert_rows_close
 from test_nsa_parity import SMALL, _edge_block_idx
 
 pytestmark = pytest.mark.gpu
@@ -126,35 +126,27 @@ def test_fsa_workspace_reuse(gpu):
         assert_lse_close(lse, rl, f"workspace reuse T={T}")
 
 
-def test_fsa_matches_query_outer_T4096_G8(gpu):
-    """B=2 Hq=32 Hkv=4 T=4096 D=128 bs=64 S=16: sampled rows against the oracle, and every
-    row within the bf16 tolerance of the query-outer kernel."""
-    c = inputs.CONFIGS["nsa_bf16_T4096_G8"]
-    q, k, v = inputs.nsa_inputs(c["B"], c["Hq"], c["Hkv"], c["T"], c["D"], seed=0)
-    idx = inputs.nsa_block_idx(c["B"], c["Hkv"], c["T"], c["block_size"], c["S"], seed=0)
-    o, lse = _run(q, k, v, idx, c["block_size"], gpu)
-    B, Hq, T, D = q.shape
-    rows = sample_rows(B, Hq, T, 3000, seed=2, extra_positions=list(range(0, 70)) + [T - 1])
-    ro, rl = oracle.nsa_ref(q, k, v, idx, c["block_size"], rows=rows)
-    assert_rows_close(o.reshape(-1, D)[rows], ro, BF16_REL, "fsa T4096 G8")
-    assert_lse_close(lse.reshape(-1)[rows], rl, "fsa T4096 G8")
-    oq, lq = cat.nsa_sel_fwd(q.to(gpu), k.to(gpu), v.to(gpu),
-                             torch.as_tensor(idx).to(gpu), c["block_size"])
+def test_fsa_matches_query_outer_T4096_G8(gpu, nsa_c4_case):
+    """B=2 Hq=32 Hkv=4 T=4096 D=128 bs=64 S=16: every element against the oracle, and
+    every row within the bf16 tolerance of the query-outer kernel."""
+    c = nsa_c4_case
+    q, k, v, idx, bs = c["q"], c["k"], c["v"], c["idx"], c["c"]["block_size"]
+    o, lse = _run(q, k, v, idx, bs, gpu)
+    assert_rows_close(o, c["ref_o"], BF16_REL, "fsa T4096 G8")
+    assert_lse_close(lse, c["ref_lse"], "fsa T4096 G8")
+    oq, lq = cat.nsa_sel_fwd(q.to(gpu), k.to(gpu), v.to(gpu), torch.as_tensor(idx).to(gpu), bs)
     torch.cuda.synchronize()
     assert_rows_close(o, oq.cpu().double().numpy(), 2 * BF16_REL, "fsa vs query-outer")
     assert_lse_close(lse, lq.cpu().double().numpy(), "fsa vs query-outer")
 
 
-def test_fsa_config_T32768_G16(gpu):
-    c = inputs.CONFIGS["nsa_bf16_T32768_G16"]
-    print("fsa T32768: inputs", flush=True)
-    q, k, v = inputs.nsa_inputs(c["B"], c["Hq"], c["Hkv"], c["T"], c["D"], seed=0)
-    idx = inputs.nsa_block_idx(c["B"], c["Hkv"], c["T"], c["block_size"], c["S"], seed=0)
+def test_fsa_config_T32768_G16(gpu, nsa_c5_case):
+    """B=1 Hq=64 Hkv=4 T=32768 D=128 bs=64 S=16: every head at every fourth query
+    position, the first 64 positions and the last one against the oracle."""
+    c = nsa_c5_case
     print("fsa T32768: gpu", flush=True)
-    o, lse = _run(q, k, v, idx, c["block_size"], gpu)
-    B, Hq, T, D = q.shape
-    rows = sample_rows(B, Hq, T, 2000, seed=3, extra_positions=(0, 63, 64, 1000, T - 1))
-    print("fsa T32768: oracle", flush=True)
-    ro, rl = oracle.nsa_ref(q, k, v, idx, c["block_size"], rows=rows)
-    assert_rows_close(o.reshape(-1, D)[rows], ro, BF16_REL, "fsa T32768 G16")
-    assert_lse_close(lse.reshape(-1)[rows], rl, "fsa T32768 G16")
+    o, lse = _run(c["q"], c["k"], c["v"], c["idx"], c["c"]["block_size"], gpu)
+    D = o.shape[-1]
+    assert_rows_close(o.reshape(-1, D)[c["rows"]], c["ref_o"], BF16_REL, "fsa T32768 G16")
+    assert_lse_close(lse.reshape(-1)[c["rows"]], c["ref_lse"], "fsa T32768 G16")
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()

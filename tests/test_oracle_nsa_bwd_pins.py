@@ -12,19 +12,23 @@ from causal_attention_tiled_amd import inputs
 
 
 def _dense_keep(idx, T, bs, G):
-    """keep[b, h, i, j]: token j is attended by query i of head h."""
+    """keep[b, h, i, j]: token j is attended by query i of head h -- the attended set
+    of the page's forward (msb-msb/openbox-llm, "nsa_selection_kernel.py",
+    `selection_forward_reference`: the tokens of the selected in-range blocks, each
+    block once, causal j <= i, shared by the G heads of a kv group), built here as a
+    Python set of token positions per (b, kv, i)."""
     B, Hkv = idx.shape[:2]
-    nblk = T // bs
-    idx_t = torch.as_tensor(idx, dtype=torch.long)
-    valid = (idx_t >= 0) & (idx_t < nblk)
-    S = idx_t.shape[-1]
-    # one row of a one-hot per slot, then "any" over the slots (padding writes nothing)
-    oh = torch.zeros(B, Hkv, T, S, nblk, dtype=torch.bool)
-    oh.scatter_(-1, idx_t.clamp(0, nblk - 1).unsqueeze(-1), valid.unsqueeze(-1))
-    chosen = oh.any(dim=3)
-    keep = chosen[..., torch.arange(T) // bs]
-    keep &= torch.tril(torch.ones(T, T, dtype=torch.bool))
-    return keep.repeat_interleave(G, dim=1)
+    keep = torch.zeros(B, Hkv * G, T, T, dtype=torch.bool)
+    for b in range(B):
+        for kv in range(Hkv):
+            for i in range(T):
+                tokens = set()
+                for blk in np.asarray(idx[b, kv, i]).tolist():
+                    if 0 <= blk < T // bs:
+                        tokens.update(j for j in range(blk * bs, (blk + 1) * bs) if j <= i)
+                if tokens:
+                    keep[b, kv * G:(kv + 1) * G, i, sorted(tokens)] = True
+    return keep
 
 
 def _autograd(q, k, v, idx, bs, do):

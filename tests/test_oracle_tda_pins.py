@@ -8,6 +8,7 @@ linearity, and a brute-force matrix evaluation on tiny inputs.
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -21,6 +22,16 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 def _f32(a):
     return torch.tensor(np.asarray(a, dtype=np.float32))
+
+
+def _normalize_f32(x):
+    """Rows of an fp32 tensor normalised under the page's reading, computed with numpy:
+    the 2-norm rounded to fp32 (at least 1e-12), then an fp32 division (correctly
+    rounded), as torch.nn.functional.normalize does on an fp32 tensor up to the
+    rounding of its own accumulation."""
+    x = x.numpy().astype(np.float32)
+    n = np.sqrt(np.sum(x.astype(np.float64) ** 2, axis=-1, keepdims=True)).astype(np.float32)
+    return (x / np.maximum(n, np.float32(1e-12))).astype(np.float64)
 
 
 def _five(B, H, T, D, seed):
@@ -71,10 +82,10 @@ def test_tda_lambda_zero_is_tra_on_path_one():
     for norm in (False, True):
         a = oracle.tda_ref(q1, q2, k1, k2, v, 0.4, 0.0, 2.0, normalize=norm)
         if norm:
-            q1n = torch.nn.functional.normalize(q1.double(), dim=-1).float()
-            k1n = torch.nn.functional.normalize(k1.double(), dim=-1).float()
+            q1n = torch.tensor(_normalize_f32(q1), dtype=torch.float32)
+            k1n = torch.tensor(_normalize_f32(k1), dtype=torch.float32)
             b = oracle.tra_ref(q1n, k1n, v, 0.4, 2.0)
-            assert np.array_equal(a, b)        # the normalised rows rounded to fp32 both ways
+            assert np.array_equal(a, b)        # the same fp32 normalised rows both ways
         else:
             assert np.array_equal(a, oracle.tra_ref(q1, k1, v, 0.4, 2.0))
 
@@ -143,12 +154,7 @@ def test_tda_brute_force_matrix_form(norm, p):
     beta, lam = 0.05 if norm else 0.3, 0.35
     got = oracle.tda_ref(q1, q2, k1, k2, v, beta, lam, p, normalize=norm)
     def nrm(x):
-        x = x.double().numpy()
-        if not norm:
-            return x
-        # normalised rows go back to the inputs' dtype (fp32 here; numpy rounds to nearest even)
-        y = x / np.maximum(np.linalg.norm(x, axis=-1, keepdims=True), 1e-12)
-        return y.astype(np.float32).astype(np.float64)
+        return _normalize_f32(x) if norm else x.double().numpy()
     Q1, Q2, K1, K2 = nrm(q1), nrm(q2), nrm(k1), nrm(k2)
     V = v.double().numpy()
     tau = beta * np.sqrt(2.0 * np.log(np.arange(T) + 1.0) / D)[:, None]
@@ -168,12 +174,105 @@ def test_tda_rows_subset_matches_full():
     assert np.array_equal(part, full[rows])
 
 
-def test_tda_normalised_bf16_rows_match_an_independent_rounding():
-    """The oracle's bf16 rounding of normalised rows (nearest, ties to even) against
-    torch's own fp64 -> bf16 conversion, through lambda = 0 and beta = 0, p = 1 where
-    the output is a plain sum of the rounded cosines times v."""
-    q1, q2, k1, k2, v = inputs.tda_inputs(2, 2, 40, 64, seed=16)
-    a = oracle.tda_ref(q1, q2, k1, k2, v, 0.0, 0.0, 1.0, normalize=True)
-    rnd = lambda x: (x.double() / x.double().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
-    b = oracle.tra_ref(rnd(q1), rnd(k1), v, 0.0, 1.0)
-    assert np.array_equal(a, b)
+def _bf16_rne(x):
+    """Exact round-to-nearest-even of a Fraction to bf16 (8 significant bits)."""
+    if x == 0:
+        return Fraction(0)
+    sgn, a = (-1 if x < 0 else 1), abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = a / Fraction(2) ** (e - 7)
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sgn * n * Fraction(2) ** (e - 7)
+
+
+def _bf16_exact_normalise(row):
+    """Exact rational evaluation of one bf16 row's normalisation: the bf16 value
+    nearest to sqrt(sum x^2), found by comparing the squares of the bf16 midpoints
+    with the exact sum, then each x / norm rounded to bf16."""
+    xs = [Fraction(float(x)) for x in row]
+    ss = sum(x * x for x in xs)
+    if ss == 0:
+        return [0.0] * len(xs)
+    c = _bf16_rne(Fraction(math.sqrt(float(ss))))
+    while True:                      # move c until sqrt(ss) lies within its rounding interval
+        e = c.numerator.bit_length() - c.denominator.bit_length()
+        while Fraction(2) ** e > c:
+            e -= 1
+        ulp = Fraction(2) ** (e - 7)
+        below = ulp / 2 if c > Fraction(2) ** e else ulp / 4   # a binade start has a finer gap below
+        lo, hi = c - below, c + ulp / 2
+        if lo * lo > ss or (lo * lo == ss and (c / ulp) % 2 == 1):
+            c -= 2 * below
+        elif hi * hi < ss or (hi * hi == ss and (c / ulp) % 2 == 1):
+            c += ulp
+        else:
+            break
+    return [float(_bf16_rne(x / c)) for x in xs]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_tda_normalised_bf16_rows_match_torch_normalize(D):
+    """The oracle's normalised bf16 rows against torch.nn.functional.normalize on the
+    same bf16 tensors, bit for bit.  torch sums the squares in fp32, so where the exact
+    norm lies within 2^-20 (relative) of a bf16 rounding midpoint its bf16 norm may fall
+    on the other side; those rows (about one in 10^3) are checked instead against an exact
+    rational evaluation of the same definition."""
+    rows_checked = ambiguous = 0
+    for seed in range(3):
+        for x in inputs.tda_inputs(1, 4, 2048, D, seed=100 + seed)[:4]:
+            got = oracle.l2norm_ref(x).reshape(-1, D)
+            want = torch.nn.functional.normalize(x, dim=-1).double().numpy().reshape(-1, D)
+            xd = x.double().reshape(-1, D).numpy()
+            nrm = np.sqrt(np.sum(xd * xd, axis=1))
+            ulp = 2.0 ** (np.floor(np.log2(nrm)) - 7)
+            near_tie = np.abs(np.mod(nrm / ulp, 1.0) - 0.5) * ulp / nrm < 2.0 ** -20
+            assert np.array_equal(got[~near_tie], want[~near_tie])
+            for r in np.nonzero(near_tie)[0]:
+                assert got[r].tolist() == _bf16_exact_normalise(x.reshape(-1, D)[r])
+            rows_checked += got.shape[0]
+            ambiguous += int(near_tie.sum())
+    assert ambiguous <= rows_checked // 400
+
+
+def test_tda_normalised_bf16_rows_hand_values():
+    """The rows of tests/golden/tda_hand_norm_rounding_T2_D2.json, worked by hand, and
+    the same rows through torch.nn.functional.normalize in bf16."""
+    with open(os.path.join(GOLDEN, "tda_hand_norm_rounding_T2_D2.json")) as f:
+        g = json.load(f)
+    for name in ("q1", "k1"):
+        x = _f32(g[name]).to(torch.bfloat16)
+        want = np.asarray(g["normalised_rows"][name])
+        assert np.array_equal(oracle.l2norm_ref(x), want)
+        assert np.array_equal(torch.nn.functional.normalize(x, dim=-1).double().numpy(), want)
+        assert [_bf16_exact_normalise(r) for r in x] == want.tolist()
+
+
+def test_tda_hand_example_norm_rounding():
+    """2-token bf16 example whose row norms are not bf16 values (worked by hand in
+    tests/golden/tda_hand_norm_rounding_T2_D2.json): rounding the norm before the
+    divide moves the normalised rows, and the output, away from the exact-quotient
+    rounding."""
+    with open(os.path.join(GOLDEN, "tda_hand_norm_rounding_T2_D2.json")) as f:
+        g = json.load(f)
+    q1, k1, q2, k2, v = (_f32(g[n]).to(torch.bfloat16)[None, None]
+                         for n in ("q1", "k1", "q2", "k2", "v"))
+    out = oracle.tda_ref(q1, q2, k1, k2, v, g["beta"], g["lambda"], g["p"], normalize=True)
+    assert np.array_equal(out[0, 0], np.asarray(g["expected"]))
+
+
+def test_tda_normalised_output_equals_tra_on_torch_normalised_rows():
+    """lambda = 0: the normalised differential forward is the rectified forward of path 1
+    on torch's bf16-normalised q1 and k1 rows (inputs chosen with no near-tie norm)."""
+    q1, q2, k1, k2, v = inputs.tda_inputs(1, 2, 150, 64, seed=17)
+    a = oracle.tda_ref(q1, q2, k1, k2, v, 0.05, 0.0, 2.0, normalize=True)
+    nq, nk = (torch.nn.functional.normalize(x, dim=-1) for x in (q1, k1))
+    assert np.array_equal(oracle.l2norm_ref(q1), nq.double().numpy())
+    assert np.array_equal(oracle.l2norm_ref(k1), nk.double().numpy())
+    assert np.array_equal(a, oracle.tra_ref(nq, nk, v, 0.05, 2.0))

@@ -9,7 +9,7 @@ import oracle
 import causal_attention_tiled_amd as cat
 from causal_attention_tiled_amd import inputs
 
-from _parity import BF16_REL, F32_REL, assert_rows_close, sample_rows
+from _parity import BF16_REL, F32_REL, assert_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -92,17 +92,16 @@ def big_tra():
     return c, q, k, v
 
 
-def test_tra_config_bf16_T8192_D128_sampled(gpu, big_tra):
-    """bf16, B=2 H=32 T=8192 D=128, beta=1, p=2 (the benchmarked launch): the full
-    output on the GPU, sampled rows (tile edges, tails, random) from the oracle."""
+def test_tra_config_bf16_T8192_D128_all_rows(gpu, big_tra):
+    """bf16, B=2 H=32 T=8192 D=128, beta=1, p=2 (the benchmarked launch): every
+    element of the GPU output against the oracle's full output."""
     c, q, k, v = big_tra
+    print("tra config T8192: gpu", flush=True)
     out = _run_bf16(q, k, v, c["beta"], 2.0, gpu)
-    B, H, T, D = q.shape
-    assert torch.isfinite(out.float()).all()
-    rows = sample_rows(B, H, T, 1500, seed=1,
-                       extra_positions=(0, 1, 31, 32, 63, 64, 127, 128, 4095, 4096, T - 2, T - 1))
-    ref = oracle.tra_ref(q, k, v, c["beta"], 2.0, rows=rows)
-    assert_rows_close(out.reshape(-1, D)[rows], ref, BF16_REL, "T8192 sampled")
+    print("tra config T8192: oracle (all 524288 rows)", flush=True)
+    ref = oracle.tra_ref(q, k, v, c["beta"], 2.0)
+    print("tra config T8192: compare", flush=True)
+    assert_rows_close(out, ref, BF16_REL, "T8192 all rows")
 
 
 @pytest.mark.parametrize("D", [64, 128])
