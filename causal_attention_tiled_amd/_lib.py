@@ -56,6 +56,10 @@ def load_library():
     lib.tda_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                             ci, ci, ci, ci, cf, cf, cf, ci, vp]
     lib.tda_fwd.restype = ci
+    lib.tda_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, cf, ci, vp]
+    lib.tda_fwd_noalloc.restype = ci
+    lib.tda_noalloc_scratch_bytes.argtypes = []
+    lib.tda_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.tda_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
     lib.tda_workspace_bytes.restype = ctypes.c_size_t
     lib.nsa_sel_fwd.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
@@ -181,6 +185,29 @@ def tda_fwd(q1, q2, k1, k2, v, beta, lam, p, normalize=True, out=None, workspace
                                 _stream_handle(stream))
     if rc != 0:
         raise AttnError("tda_fwd", rc)
+    return out
+
+
+def tda_noalloc_scratch_bytes() -> int:
+    """Bytes of the static scratch that tda_fwd_noalloc uses (its size limit)."""
+    return int(load_library().tda_noalloc_scratch_bytes())
+
+
+def tda_fwd_noalloc(q1, q2, k1, k2, v, beta, lam, p, *, out, normalize=True, stream=None):
+    """tda_fwd for callers that cannot allocate: the library keeps the normalised key
+    rows in its own static scratch on the current GPU (calls that may overlap in time on
+    one GPU race).  ``out`` (bfloat16, q1's shape) must be given.  Returns ``out``."""
+    for t, n in ((q1, "q1"), (q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v"), (out, "out")):
+        _check(t, n, torch.bfloat16)
+    if q1.dim() != 4 or any(t.shape != q1.shape for t in (q2, k1, k2, v, out)):
+        raise ValueError("q1, q2, k1, k2, v, out must all be [B, H, T, D]")
+    B, H, T, D = q1.shape
+    rc = load_library().tda_fwd_noalloc(q1.data_ptr(), q2.data_ptr(), k1.data_ptr(),
+                                        k2.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, T, D,
+                                        float(beta), float(lam), float(p),
+                                        1 if normalize else 0, _stream_handle(stream))
+    if rc != 0:
+        raise AttnError("tda_fwd_noalloc", rc)
     return out
 
 

@@ -1,10 +1,13 @@
 // attn_api.hip -- the C ABI of libattn.so (declared in include/attn.h).
 //
 // Every argument is validated on the host before any HIP call; then the kernel is
-// launched asynchronously on the caller's stream.  Nothing is allocated, nothing is
-// synchronised, no state is kept between calls.
+// launched asynchronously on the caller's stream.  Nothing is allocated and nothing is
+// synchronised; the only state kept between calls is tda_fwd_noalloc's static scratch
+// array and its address on each device.
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "attn.h"
 #include "attn_internal.h"
@@ -118,22 +121,25 @@ ATTN_EXPORT size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize
     return (size_t)2 * (size_t)B * (size_t)H * (size_t)T * (size_t)D * 2;
 }
 
-ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const void *k2,
-                        const void *v, void *out, void *workspace, size_t workspace_bytes,
-                        int B, int H, int T, int D, float beta, float lambda, float p,
-                        int normalize, void *stream) {
+namespace {
+
+// Checks of tda_fwd's arguments other than the workspace; *noop for an empty problem.
+int tda_validate(const void *q1, const void *q2, const void *k1, const void *k2, const void *v,
+                 const void *out, int B, int H, int T, int D, float beta, float lambda, float p,
+                 bool *noop) {
+    *noop = false;
     if (!isfinite(lambda)) return ATTN_ERR_SHAPE;
-    bool noop;
-    const int st = tra_validate(q1, k1, v, out, B, H, T, D, beta, p, attn::kTdaRows, &noop);
-    if (st != ATTN_OK || noop) return st;
+    const int st = tra_validate(q1, k1, v, out, B, H, T, D, beta, p, attn::kTdaRows, noop);
+    if (st != ATTN_OK || *noop) return st;
     if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     if (!q2 || !k2) return ATTN_ERR_NULL;
     if (misaligned(q2) || misaligned(k2)) return ATTN_ERR_ALIGN;
-    const size_t need = tda_workspace_bytes(B, H, T, D, normalize);
-    if (need > 0) {
-        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-        if (misaligned(workspace)) return ATTN_ERR_ALIGN;
-    }
+    return ATTN_OK;
+}
+
+int tda_launch(const void *q1, const void *q2, const void *k1, const void *k2, const void *v,
+               void *out, void *workspace, int B, int H, int T, int D, float beta,
+               float lambda, float p, int normalize, void *stream) {
     const hipError_t e = attn::launch_tda_fwd_bf16(
         static_cast<const uint16_t *>(q1), static_cast<const uint16_t *>(q2),
         static_cast<const uint16_t *>(k1), static_cast<const uint16_t *>(k2),
@@ -141,6 +147,70 @@ ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const vo
         static_cast<uint16_t *>(workspace), B * H, T, D, beta, lambda, p, normalize ? 1 : 0,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+// Scratch memory of tda_fwd_noalloc: the normalised k1 and k2 rows.  Every GPU the
+// library runs on holds its own copy of this array, at its own address, until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels take the address that hipGetSymbolAddress returns for the current
+// device, kept per device in scratch_dev.
+constexpr size_t kTdaScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kTdaScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_dev[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device,
+// on the first call made with that device current.
+int scratch_ptr(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return ATTN_ERR_LAUNCH;
+        scratch_dev[dev] = p;
+    }
+    *ptr = scratch_dev[dev];
+    return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_EXPORT int tda_fwd(const void *q1, const void *q2, const void *k1, const void *k2,
+                        const void *v, void *out, void *workspace, size_t workspace_bytes,
+                        int B, int H, int T, int D, float beta, float lambda, float p,
+                        int normalize, void *stream) {
+    bool noop;
+    const int st = tda_validate(q1, q2, k1, k2, v, out, B, H, T, D, beta, lambda, p, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const size_t need = tda_workspace_bytes(B, H, T, D, normalize);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+        if (misaligned(workspace)) return ATTN_ERR_ALIGN;
+    }
+    return tda_launch(q1, q2, k1, k2, v, out, workspace, B, H, T, D, beta, lambda, p, normalize,
+                      stream);
+}
+
+ATTN_EXPORT size_t tda_noalloc_scratch_bytes(void) { return kTdaScratchBytes; }
+
+ATTN_EXPORT int tda_fwd_noalloc(const void *q1, const void *q2, const void *k1, const void *k2,
+                                const void *v, void *out, int B, int H, int T, int D,
+                                float beta, float lambda, float p, int normalize, void *stream) {
+    bool noop;
+    const int st = tda_validate(q1, q2, k1, k2, v, out, B, H, T, D, beta, lambda, p, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const size_t need = tda_workspace_bytes(B, H, T, D, normalize);
+    if (need > kTdaScratchBytes) return ATTN_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        const int sst = scratch_ptr(&ws);
+        if (sst != ATTN_OK) return sst;
+    }
+    return tda_launch(q1, q2, k1, k2, v, out, ws, B, H, T, D, beta, lambda, p, normalize, stream);
 }
 
 ATTN_EXPORT int nsa_sel_fwd(const void *q, const void *k, const void *v,
@@ -235,6 +305,7 @@ ATTN_EXPORT const char *attn_status_str(int status) {
         case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
         case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATTN_ERR_SCRATCH: return "problem needs more than the library's static scratch holds";
         default: return "unknown status";
     }
 }

@@ -6,7 +6,8 @@
  * ----------------------------------
  *  - Every tensor pointer is a DEVICE pointer to memory the caller owns and
  *    keeps alive until the work on `stream` has finished.  The library never
- *    allocates, frees, or keeps a pointer after returning.
+ *    allocates, frees, or keeps a pointer after returning (tda_fwd_noalloc
+ *    uses a static device array that the library itself carries).
  *  - Tensors are dense and row-major (contiguous) in the shapes given below;
  *    "bf16" means IEEE bfloat16 stored as 16-bit words.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
@@ -18,7 +19,8 @@
  *    bf16 kernels address within one slab of T x D elements with 32-bit byte
  *    offsets, so every bf16 entry point requires T * D * 2 < 2^31 (T < 2^23
  *    at D = 128, T < 2^24 at D = 64), else ATTN_ERR_UNSUPPORTED.
- *  - The library is stateless and may be called from several host threads.
+ *  - The library is stateless (apart from tda_fwd_noalloc's scratch) and may
+ *    be called from several host threads.
  *  - A size of zero in B, H/Hq or T is a successful no-op once the other
  *    arguments have been validated; the tensor pointers may then be NULL.
  *
@@ -42,6 +44,7 @@ extern "C" {
 #define ATTN_ERR_ALIGN (-4)       /* a tensor pointer is not 16-byte aligned */
 #define ATTN_ERR_LAUNCH (-5)      /* the HIP launch reported an error */
 #define ATTN_ERR_WORKSPACE (-6)   /* workspace missing or smaller than required */
+#define ATTN_ERR_SCRATCH (-7)     /* needs more than the library's static scratch holds */
 
 /*
  * Threshold Rectified Attention forward, bf16 in / bf16 out.
@@ -149,6 +152,37 @@ int tda_fwd(const void *q1, const void *q2, const void *k1, const void *k2, cons
 /* Workspace bytes tda_fwd needs for these sizes (0 when normalize == 0, or
  * when a size is negative or zero). */
 size_t tda_workspace_bytes(int B, int H, int T, int D, int normalize);
+
+/*
+ * tda_fwd without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same definition, arguments (minus the workspace), numerics
+ * and errors as tda_fwd, and the same kernels.
+ *
+ * The normalised k1 and k2 rows go to a static scratch array inside the library
+ * (tda_noalloc_scratch_bytes() = 64 MiB), which every GPU the library runs on
+ * holds until the process ends; its address on the current device is looked up
+ * on the first call made with that device current (a HIP runtime query, no
+ * allocation).  Nothing is allocated or freed by any call.
+ *
+ *   limit   : tda_workspace_bytes(B, H, T, D, normalize) <= 64 MiB, i.e.
+ *             B*H*T*D <= 2^24 elements when normalising (else ATTN_ERR_SCRATCH);
+ *             without normalisation no scratch is used and there is no limit.
+ *   device  : the current HIP device; `stream` must belong to it.
+ *   sharing : all calls on one GPU share that GPU's scratch, which keeps the last
+ *             call's contents (each call overwrites every byte it reads), so calls
+ *             whose work may overlap in time on one GPU -- on different streams, or
+ *             from several host threads -- race and must be serialised by the
+ *             caller.  Calls on one stream are ordered and safe.
+ *   errors  : as tda_fwd; ATTN_ERR_SCRATCH as above; ATTN_ERR_LAUNCH also when
+ *             the scratch address cannot be looked up.
+ */
+int tda_fwd_noalloc(const void *q1, const void *q2, const void *k1, const void *k2, const void *v,
+                    void *out, int B, int H, int T, int D, float beta, float lambda, float p,
+                    int normalize, void *stream);
+
+/* Bytes of the static scratch tda_fwd_noalloc uses (its size limit). */
+size_t tda_noalloc_scratch_bytes(void);
 
 /*
  * NSA selection-branch forward, bf16 in / bf16 out, fp32 lse.

@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 P = 0x10000  # a 16-byte aligned dummy address (never touched by validation)
 
 
@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tra_fwd", "tra_fwd_f32", "tra_bwd", "tda_fwd", "tda_workspace_bytes",
               "nsa_sel_fwd", "nsa_sel_bwd", "nsa_sel_bwd_workspace_bytes", "nsa_sel_fwd_fsa",
-              "nsa_sel_fsa_workspace_bytes", "attn_status_str"):
+              "nsa_sel_fsa_workspace_bytes", "tda_fwd_noalloc", "tda_noalloc_scratch_bytes",
+              "attn_status_str"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     import causal_attention_tiled_amd as cat
-    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK):
+    for code in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, ELAUNCH, EWORK, ESCRATCH):
         assert cat.attn_status_str(code) not in ("", "unknown status")
     assert cat.attn_status_str(12345) == "unknown status"
 
@@ -220,3 +221,28 @@ def test_bf16_slab_byte_limit(lib, D, T):
     assert _nsa(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP
     assert _nbwd(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP
     assert _fsa(lib, T=T, D=D, Hq=2, Hkv=2) == EUNSUP
+
+
+def _tdan(lib, q1=P, q2=P, k1=P, k2=P, v=P, o=P, B=1, H=1, T=8, D=128, beta=0.1, lam=0.5, p=2.0,
+          norm=1):
+    return lib.tda_fwd_noalloc(q1, q2, k1, k2, v, o, B, H, T, D, beta, lam, p, norm, None)
+
+
+def test_tda_noalloc_validation(lib):
+    """tda_fwd_noalloc: tda_fwd's checks, and a problem whose normalised keys exceed the
+    static scratch is refused before any HIP call."""
+    cap = lib.tda_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    assert _tdan(lib, q2=None) == ENULL
+    assert _tdan(lib, o=None) == ENULL
+    assert _tdan(lib, T=-1) == ESHAPE
+    assert _tdan(lib, lam=float("nan")) == ESHAPE
+    assert _tdan(lib, p=0.0) == ESHAPE
+    assert _tdan(lib, D=96) == EUNSUP
+    assert _tdan(lib, k1=P + 8) == EALIGN
+    assert _tdan(lib, T=1 << 23) == EUNSUP
+    # 2 * B*H*T*D * 2 bytes of normalised keys: 2^24 elements fit exactly, one row more does not
+    assert lib.tda_workspace_bytes(1, 16, 8192, 128, 1) == cap
+    assert _tdan(lib, B=1, H=16, T=8193, D=128) == ESCRATCH
+    assert _tdan(lib, B=2, H=32, T=8192, D=128) == ESCRATCH
+    assert _tdan(lib, q1=None, q2=None, k1=None, k2=None, v=None, o=None, T=0) == OK
