@@ -341,9 +341,9 @@ def measured_ceilings():
         res[name] = probes.read_bandwidth(nbytes)
     res["mfma_bf16_tflops"], res["sclk_ghz_under_mfma"] = probes.mfma_rate()
     res["log_exp_lane_ops_per_s"] = probes.transcendental_rate()
-    res["note"] = ("read: 16-byte loads by 2048 workgroups of 256 threads, each re-reading "
-                   "its own elements, of 16 MiB (L2-resident), 128 MiB (MALL-resident) and "
-                   "4 GiB (HBM); mfma: 4 chains of v_mfma_f32_32x32x16_bf16 per wave, 8 waves "
+    res["note"] = ("read: 16-byte loads by 2048 workgroups of 256 threads, each XCD "
+                   "re-reading its own contiguous eighth, of 16 MiB (L2-resident), 128 MiB "
+                   "(MALL-resident) and 4 GiB (HBM); mfma: 4 chains of v_mfma_f32_32x32x16_bf16 per wave, 8 waves "
                    "per CU, clock = shader cycles (s_memtime) over 100 MHz ticks "
                    "(s_memrealtime); log/exp: 8 chains of v_log_f32, v_exp_f32 per lane")
     return res

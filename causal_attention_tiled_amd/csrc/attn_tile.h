@@ -18,8 +18,10 @@ __device__ __forceinline__ float relu_pow(float x, float p) {
         const float r = fmaxf(x, 0.0f);
         return r * r;
     } else {
-        // x^p = 2^(p log2 x) for x > 0 (v_log_f32 / v_exp_f32 are base 2).
-        return x > 0.0f ? __builtin_amdgcn_exp2f(p * __builtin_amdgcn_logf(x)) : 0.0f;
+        // x^p = 2^(p log2 x) for x > 0 (v_log_f32 / v_exp_f32 are base 2).  For x <= 0
+        // (and the -inf of masked keys) max(x, 0) = 0, log2(0) = -inf and, as p > 0,
+        // 2^(p * -inf) = 0 exactly: no compare and select.
+        return __builtin_amdgcn_exp2f(p * __builtin_amdgcn_logf(fmaxf(x, 0.0f)));
     }
 }
 

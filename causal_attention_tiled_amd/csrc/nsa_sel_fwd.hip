@@ -14,8 +14,11 @@
 //    per group, not once per head.
 //  * The S slots of the query's block_idx row are validated lane-parallel (lane s
 //    holds slot s): padding, ids past T/bs, blocks after i and repeats of an earlier
-//    slot are dropped, and the survivors form a bit mask that the wave walks.  No
-//    scan over the KV sequence takes place.
+//    slot are dropped, and the wave walks the survivors in decreasing block order.
+//    No scan over the KV sequence takes place.  The order only changes the rounding
+//    order of the online softmax; it makes the waves that run together on an XCD read
+//    nearby blocks at the same time (their k-th largest), which at T = 32768 G = 16
+//    keeps enough of the gathers in L2 to cut the time by a fifth against slot order.
 //  * Keys are processed in chunks of 32, with one K tile and one V tile of LDS per
 //    wave.  Both go from HBM straight into LDS (buffer loads with the LDS as
 //    destination), each 1 KB instruction moving whole rows (4 rows at D = 128): K
@@ -133,7 +136,20 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
         const int other = __builtin_amdgcn_readlane(myblk, s2);
         keep = keep && !(s2 < lane && other == myblk);
     }
-    uint64_t rem = __builtin_amdgcn_ballot_w64(keep);
+    // The kept blocks are visited in decreasing block order: lane s's rank is the
+    // number of kept blocks above its own (the kept blocks are distinct, so the ranks
+    // are 0 .. nkept-1).  Waves of neighbouring queries run at the same time and reach
+    // their k-th largest blocks together, so the blocks read across an XCD at any
+    // moment lie close together and more of them are still in its L2; in slot order
+    // (random) the whole causal prefix is in use at once.
+    const uint64_t kept = __builtin_amdgcn_ballot_w64(keep);
+    const int nkept = __builtin_popcountll(kept);
+    int rank = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+        const int other = __builtin_amdgcn_readlane(myblk, s2);
+        rank += (int)(((kept >> s2) & 1) != 0 && other > myblk);
+    }
+    int taken = 0;
 
     // Q^T operand: head kv*G + n16 (zero for n16 >= G), dims 32*ds + 8*g4 .. +7
     const bool head_ok = n16 < G;
@@ -229,9 +245,9 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
             ++cur_c;
             return cur_blk * BS + cur_c * kChunk;
         }
-        if (rem == 0) return -1;
-        const int s = __builtin_ctzll(rem);
-        rem &= rem - 1;
+        if (taken == nkept) return -1;
+        const int s = __builtin_ctzll(__builtin_amdgcn_ballot_w64(keep && rank == taken));
+        ++taken;
         cur_blk = __builtin_amdgcn_readlane(myblk, s);
         cur_c = 0;
         return cur_blk * BS;

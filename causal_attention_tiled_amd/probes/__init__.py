@@ -2,9 +2,10 @@
 built next to libattn.so by ``causal_attention_tiled_amd.build``; not part of the
 attention library's C ABI).
 
-``read_bandwidth(nbytes)``  streaming read GB/s of a buffer of nbytes: 16 MiB is
-                            served by the XCDs' L2s, 128 MiB by the memory-side cache
-                            (MALL), 4 GiB by HBM.
+``read_bandwidth(nbytes)``  streaming read GB/s of a buffer of nbytes, each XCD reading
+                            its own contiguous eighth: 16 MiB (2 MiB per XCD) is served by
+                            the XCDs' L2s, 128 MiB (16 MiB per XCD) by the memory-side
+                            cache (MALL), 4 GiB by HBM.
 ``mfma_rate()``             bf16 MFMA TFLOP/s (v_mfma_f32_32x32x16_bf16 chains) and the
                             engine clock observed meanwhile (GHz).
 ``transcendental_rate()``   v_log_f32 + v_exp_f32 instructions per second (lane ops).

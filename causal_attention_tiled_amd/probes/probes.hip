@@ -1,10 +1,10 @@
 // probes.hip -- microbenchmarks that measure ceilings of the MI355X for the rooflines
 // reported next to the attention kernels (built into libprobes.so, not into
 // libattn.so; bench.py and the profiling runs load it):
-//  * read_kernel: streaming 16-byte loads over a buffer, each workgroup always reading
-//    the same elements, so that a buffer sized under the L2 of the reading XCD (4 MiB
-//    each) is served by L2, one sized between the L2s and the memory-side cache (MALL,
-//    256 MiB) by the MALL, and a larger one by HBM;
+//  * read_kernel: streaming 16-byte loads over a buffer, each XCD always reading its own
+//    contiguous eighth, so that a buffer whose eighth fits an XCD's L2 (4 MiB) is
+//    served by L2, one whose eighth exceeds it but that fits the memory-side cache
+//    (MALL, 256 MiB) by the MALL, and a larger one by HBM;
 //  * mfma_kernel: independent chains of v_mfma_f32_32x32x16_bf16, timed by the shader
 //    clock counter (s_memtime) and the constant 100 MHz counter (s_memrealtime) on
 //    each wave, whose ratio is the engine clock under MFMA load;
@@ -24,23 +24,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t kNever = 0x9e3779b9u;  // a value the reductions below practically never take
 
-// n elements of 16 bytes; thread (workgroup w, lane t) reads elements w*256 + t + k*stride
-// in every pass, four loads in flight per thread.
+// n elements of 16 bytes (n a multiple of 8), grid a multiple of 8.  Workgroups are
+// dealt to the 8 XCDs round-robin, so workgroup w runs on XCD w % 8; the workgroups of
+// XCD x read the contiguous eighth x of the buffer, thread t of the XCD's workgroup
+// number w / 8 reading its elements t + k*stride in every pass (four loads in flight).
 __global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ buf, int64_t n,
                                                    int passes, uint32_t *__restrict__ sink) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    const int64_t first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t per_xcd = n / 8;
+    const u32x4 *part = buf + (int64_t)(blockIdx.x & 7) * per_xcd;
+    const int64_t stride = (int64_t)(gridDim.x / 8) * 256;
+    const int64_t first = (int64_t)(blockIdx.x >> 3) * 256 + threadIdx.x;
     uint32_t acc = 0;
     for (int p = 0; p < passes; ++p) {
         int64_t i = first;
-        for (; i + 3 * stride < n; i += 4 * stride) {
-            const u32x4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride],
-                        d = buf[i + 3 * stride];
+        for (; i + 3 * stride < per_xcd; i += 4 * stride) {
+            const u32x4 a = part[i], b = part[i + stride], c = part[i + 2 * stride],
+                        d = part[i + 3 * stride];
             const u32x4 x = a ^ b ^ c ^ d;
             acc ^= x.x ^ x.y ^ x.z ^ x.w;
         }
-        for (; i < n; i += stride) {
-            const u32x4 a = buf[i];
+        for (; i < per_xcd; i += stride) {
+            const u32x4 a = part[i];
             acc ^= a.x ^ a.y ^ a.z ^ a.w;
         }
     }
@@ -99,11 +103,12 @@ __global__ __launch_bounds__(256) void trans_kernel(int iters, float *__restrict
 
 }  // namespace
 
-// Streaming read of `bytes` (a multiple of 16) at `buf`, `passes` times, by `grid`
-// workgroups of 256 threads.  Returns the HIP launch status.
+// Streaming read of `bytes` (a multiple of 128) at `buf`, `passes` times, by `grid`
+// workgroups of 256 threads (a multiple of 8).  Returns the HIP launch status.
 PROBE_EXPORT int probe_read(const void *buf, int64_t bytes, int passes, int grid, void *sink,
                             void *stream) {
-    if (!buf || !sink || bytes < 16 || (bytes & 15) || passes < 1 || grid < 1) return -1;
+    if (!buf || !sink || bytes < 128 || (bytes & 127) || passes < 1 || grid < 8 || (grid & 7))
+        return -1;
     hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const u32x4 *)buf, bytes / 16, passes, (uint32_t *)sink);
     return (int)hipGetLastError();
