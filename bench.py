@@ -476,10 +476,13 @@ def main():
                          "L2 and the memory-side cache, so not a fraction of HBM bandwidth"})
     dominant = roof_nsa if nsa_avg >= tra_avg else roof_tra
     ceilings = measured_ceilings() if not args.no_ceilings else None
-    if ceilings is not None and roof_nsa.get("traffic") and run_nsa:
-        rate = roof_nsa["traffic"] / (nsa_avg * 1e-3) / 1e9
-        roof_nsa["l2_miss_gbps"] = rate
-        roof_nsa["l2_miss_frac_of_mall_read_ceiling"] = rate / ceilings["read_mall_gbps"]
+    if ceilings is not None and run_nsa:
+        # every gathered byte passes from L2 to the CUs: the measured L2 read rate bounds it
+        roof_nsa["gathered_frac_of_l2_read_ceiling"] = nsa_gbps / ceilings["read_l2_gbps"]
+        if roof_nsa.get("traffic"):
+            rate = roof_nsa["traffic"] / (nsa_avg * 1e-3) / 1e9
+            roof_nsa["l2_miss_gbps"] = rate
+            roof_nsa["l2_miss_frac_of_mall_read_ceiling"] = rate / ceilings["read_mall_gbps"]
 
     result = {
         "metric": METRIC,

@@ -419,14 +419,19 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
             for (int j = 0; j < 4; ++j) sinit[4 * g + j] = t4[j];
         }
     };
-    for (int n = n0; n < ntiles; ++n) {
-        const int buf = (n - n0) & 1;
+    // One tile of 64 queries (two blocks).  Only the workgroup's first two tiles hold
+    // blocks before or at a wave's diagonal block (the masked form); the rest run
+    // mask-free, two tiles at a time so that every LDS buffer offset is a constant.
+    auto tile = [&](int n, auto masked, int buf) {
+        constexpr bool kMasked = decltype(masked)::value;
         if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
         bool have_q = false;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int jb = 2 * n + qb;  // global 32-query block
-            if (jb < jd) continue;      // every query of the block precedes every key of the wave
+            if constexpr (kMasked) {
+                if (jb < jd) continue;  // every query of the block precedes every key of the wave
+            }
             if (!have_q) read_q(buf, qb);
             // 1
             f32x16 s = sinit;
@@ -440,7 +445,9 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (jb == jd) mask_diag(s);
+            if constexpr (kMasked) {
+                if (jb == jd) mask_diag(s);
+            }
             // 2
             f32x16 dp = zero16;
             bf16x8 wf[2];
@@ -500,7 +507,17 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0x0070);
         __builtin_amdgcn_s_barrier();
+    };
+    const std::true_type masked{};
+    const std::false_type plain{};
+    tile(n0, masked, 0);
+    if (n0 + 1 < ntiles) tile(n0 + 1, masked, 1);
+    int n = n0 + 2;
+    for (; n + 1 < ntiles; n += 2) {
+        tile(n, plain, 0);
+        tile(n + 1, plain, 1);
     }
+    if (n < ntiles) tile(n, plain, 0);
 
     // dK^T, dV^T accumulators: lane holds key kw0 + l32, dims 32*dt + 8*i + 4*hi + j.
     if (mykey < T) {

@@ -8,6 +8,8 @@ attention library's C ABI).
                             cache (MALL), 4 GiB by HBM.
 ``mfma_rate()``             bf16 MFMA TFLOP/s (v_mfma_f32_32x32x16_bf16 chains) and the
                             engine clock observed meanwhile (GHz).
+``mfma_chain_rate(chains)``  bf16 MFMA TFLOP/s of one wave per SIMD running 1, 2 or 4
+                            independent chains of dependent MFMAs.
 ``transcendental_rate()``   v_log_f32 + v_exp_f32 instructions per second (lane ops).
 """
 from __future__ import annotations
@@ -31,6 +33,8 @@ def _load():
         lib.probe_read.argtypes = [vp, i64, ctypes.c_int, ctypes.c_int, vp, vp]
         lib.probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
         lib.probe_trans.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+        lib.probe_mfma_chains.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+        lib.probe_mfma_chains.restype = ctypes.c_int
         for f in (lib.probe_read, lib.probe_mfma, lib.probe_trans):
             f.restype = ctypes.c_int
         _lib = lib
@@ -92,6 +96,23 @@ def mfma_rate(iters: int = 20000, reps: int = 3):
     c = clk.view(-1, 2).double()
     ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
     return flops / (ms * 1e-3) / 1e12, ghz
+
+
+def mfma_chain_rate(chains: int, iters: int = 20000, reps: int = 3) -> float:
+    """bf16 TFLOP/s of one wave per SIMD (1024 single-wave workgroups) running `chains`
+    independent chains of dependent 32x32x16 MFMAs."""
+    import torch
+    lib = _load()
+    grid = 4 * _CUS
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        rc = lib.probe_mfma_chains(iters, chains, grid, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_mfma_chains failed: {rc}")
+    ms = _time_ms(launch, reps)
+    return 32768.0 * iters * chains * grid / (ms * 1e-3) / 1e12
 
 
 def transcendental_rate(iters: int = 4000, reps: int = 3) -> float:

@@ -8,6 +8,8 @@
 //  * mfma_kernel: independent chains of v_mfma_f32_32x32x16_bf16, timed by the shader
 //    clock counter (s_memtime) and the constant 100 MHz counter (s_memrealtime) on
 //    each wave, whose ratio is the engine clock under MFMA load;
+//  * mfma_chain_kernel: one wave per SIMD running 1, 2 or 4 independent chains of
+//    dependent MFMAs, to measure how fast a dependent MFMA issues behind its predecessor;
 //  * trans_kernel: independent chains of v_log_f32 followed by v_exp_f32 (the pair the
 //    general-power epilogue x^p = exp2(p log2 x) issues per element).
 // Every loop is bounded by its arguments and every access stays inside its buffer.
@@ -84,6 +86,33 @@ __global__ __launch_bounds__(256) void mfma_kernel(int iters, float *__restrict_
     }
 }
 
+// One wave per SIMD (a single-wave workgroup, one workgroup per SIMD of the chip) running
+// CH independent chains of dependent v_mfma_f32_32x32x16_bf16 (each accumulating into its
+// own registers), to see how fast back-to-back dependent MFMAs issue.
+template <int CH>
+__global__ __launch_bounds__(64) void mfma_chain_kernel(int iters, float *__restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        a[t] = (__bf16)(0.001f * (float)(lane + t));
+        b[t] = (__bf16)(0.002f * (float)(lane - t));
+    }
+    f32x16 c[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) c[j] = f32x16{};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += c[j][r];
+    if (s == 1234.5f) sink[0] = s;
+}
+
 // Eight independent chains per lane of x <- 2^-|log2 |x||, which stays in (0, 1]:
 // each step is one v_log_f32 and one v_exp_f32 with input modifiers only.
 __global__ __launch_bounds__(256) void trans_kernel(int iters, float *__restrict__ sink) {
@@ -120,6 +149,21 @@ PROBE_EXPORT int probe_mfma(int iters, int grid, void *sink, void *clk, void *st
     if (!sink || !clk || iters < 1 || grid < 1) return -1;
     hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
                        (float *)sink, (uint64_t *)clk);
+    return (int)hipGetLastError();
+}
+
+// `iters` MFMAs per chain, `chains` (1, 2 or 4) independent chains per wave, one wave per
+// workgroup, `grid` workgroups.
+PROBE_EXPORT int probe_mfma_chains(int iters, int chains, int grid, void *sink, void *stream) {
+    if (!sink || iters < 1 || grid < 1) return -1;
+    if (chains == 1)
+        hipLaunchKernelGGL(mfma_chain_kernel<1>, dim3(grid), dim3(64), 0, (hipStream_t)stream, iters, (float *)sink);
+    else if (chains == 2)
+        hipLaunchKernelGGL(mfma_chain_kernel<2>, dim3(grid), dim3(64), 0, (hipStream_t)stream, iters, (float *)sink);
+    else if (chains == 4)
+        hipLaunchKernelGGL(mfma_chain_kernel<4>, dim3(grid), dim3(64), 0, (hipStream_t)stream, iters, (float *)sink);
+    else
+        return -1;
     return (int)hipGetLastError();
 }
 
