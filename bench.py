@@ -259,7 +259,8 @@ def extra_configs(dev, nsa_c5=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
-    at T=4096 (forward, block-outer forward and backward); and NSA G=16 at T=32768:
+    at T=4096 (forward, block-outer forward and backward); both NSA forwards at Hq=16
+    T=8192 for G = 1, 2, 4, 8, 16; and NSA G=16 at T=32768:
     block-outer forward, backward, and forward with L2 and MALL flushed before every
     launch."""
     res = {}
@@ -314,6 +315,21 @@ def extra_configs(dev, nsa_c5=None):
     res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv,
                        "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
     del qn, kn, vn, gidx, o, lse
+    # which NSA forward to call: both forms at B1 Hq16 T8192 D128 bs64 S16 over G = Hq/Hkv
+    B, Hq, T, D, bs, S = 1, 16, 8192, 128, 64, 16
+    for Hkv in (16, 8, 4, 2, 1):
+        qn, kn, vn = (x.to(dev) for x in inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0))
+        idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
+        gidx = torch.from_numpy(idx).to(dev)
+        o = torch.empty_like(qn)
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+        gb = nsa_gathered_bytes(idx, T, bs, D)
+        st = timed(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), 5, 10, 20)
+        shape = f"B1 Hq16 Hkv{Hkv} (G={Hq // Hkv}) T8192 D128 bs64 S16"
+        res[f"nsa_sel_fwd {shape}"] = dict(st, gathered_gb=gb / 1e9,
+                                           gbps=gb / (st["ms"] * 1e-3) / 1e9)
+        res.update(nsa_fsa(dev, qn, kn, vn, gidx, bs, gb, f"nsa_sel_fwd_fsa (block-outer) {shape}"))
+        del qn, kn, vn, gidx, o, lse
     if nsa_c5 is not None:
         fn, gb, t5 = nsa_c5
         res.update(nsa_fsa(dev, *t5[:5], gb,

@@ -6,8 +6,9 @@
 // per (group = batch*Hkv + kv head, block) the increasing list of queries that attend
 // the block (a listed block that is valid, not after the query's own block; a repeat
 // counts once).  Built each call from block_idx, with no host round trip:
-//  1. a bitmap per (group, block) over the query positions, set with atomic ORs (a
-//     repeated slot sets the same bit again, so duplicates vanish);
+//  1. a bitmap per (group, block) over the query positions, built per 32-query word in
+//     an LDS hash table keyed by block (a repeated slot sets the same bit again, so
+//     duplicates vanish) and stored word by word;
 //  2. popcount per list; 3. one workgroup scans the counts into list offsets;
 //  4. one wave per list writes the positions of its set bits in order, and for each
 //     32-bit word the list position of its first set bit;
@@ -24,19 +25,49 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     if (i < n) p[i] = 0u;
 }
 
-// one thread per (group, query, slot): set bit i of the (group, block) bitmap
+// one workgroup per (group, 32-query word w): the listed blocks of the word's queries go
+// into an LDS hash table (open addressing on the block id, at least twice as many entries
+// as the word has slots, so a probe always ends), each entry ORing in its queries' bits;
+// then every entry is stored as word w of its block's bitmap.  Word w of a group's lists
+// has this one writer, so plain stores suffice (the words no query lists stay zero).
+constexpr int kHashMax = 4096;  // entries for S = 64: 2 * 32 * 64
+
 __global__ __launch_bounds__(256) void csr_bitmap_kernel(const int32_t *__restrict__ idx,
                                                          uint32_t *__restrict__ bits, int T,
                                                          int S, int nblk, int bs, int words,
-                                                         int64_t total) {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
-    const int blk = idx[e];
-    const int64_t row = e / S;                // (group, i)
-    const int i = (int)(row % T);
-    const int64_t group = row / T;
-    if (blk < 0 || blk >= nblk || blk * bs > i) return;
-    atomicOr(&bits[(group * nblk + blk) * words + (i >> 5)], 1u << (i & 31));
+                                                         int tbits) {
+    __shared__ int key[kHashMax];
+    __shared__ uint32_t val[kHashMax];
+    const int tsize = 1 << tbits;
+    const int64_t group = blockIdx.x / words;
+    const int w = (int)(blockIdx.x % words);
+    for (int k = threadIdx.x; k < tsize; k += 256) {
+        key[k] = -1;
+        val[k] = 0u;
+    }
+    __syncthreads();
+    const int i0 = w * 32;
+    const int n = min(32, T - i0) * S;
+    const int32_t *src = idx + (group * T + i0) * S;
+    for (int e = threadIdx.x; e < n; e += 256) {
+        const int blk = src[e];
+        const int i = i0 + e / S;
+        if (blk < 0 || blk >= nblk || blk * bs > i) continue;
+        int h = (int)(((uint32_t)blk * 2654435761u) >> (32 - tbits));
+        while (true) {
+            const int prev = atomicCAS(&key[h], -1, blk);
+            if (prev == -1 || prev == blk) {
+                atomicOr(&val[h], 1u << (i & 31));
+                break;
+            }
+            h = (h + 1) & (tsize - 1);
+        }
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < tsize; k += 256) {
+        const int blk = key[k];
+        if (blk >= 0) bits[(group * nblk + blk) * words + w] = val[k];
+    }
 }
 
 // one wave per (group, block): number of attending queries
@@ -198,9 +229,10 @@ hipError_t nsa_index_build(const NsaIndex &ix, const int32_t *idx, int B, int Hk
         if (e != hipSuccess) return e;
     }
     {
-        int64_t total = (int64_t)B * Hkv * T * S;
-        void *a[] = {&idx, &bits, &T, &S, &nblk, &bs, &words, &total};
-        e = hipLaunchKernel((const void *)csr_bitmap_kernel, dim3((unsigned)((total + 255) / 256)),
+        int tbits = 8;  // table entries: a power of two >= 2 * 32 * S
+        while ((1 << tbits) < 64 * S) ++tbits;
+        void *a[] = {&idx, &bits, &T, &S, &nblk, &bs, &words, &tbits};
+        e = hipLaunchKernel((const void *)csr_bitmap_kernel, dim3((unsigned)((int64_t)B * Hkv * words)),
                             dim3(256), a, 0, stream);
         if (e != hipSuccess) return e;
     }

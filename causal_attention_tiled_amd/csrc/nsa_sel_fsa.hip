@@ -19,9 +19,11 @@
 //    after the query, own block only), the block-local row max m and sum l, P in bf16 in
 //    accumulator order as the B operand of O^T += V^T P^T (V^T by transposing LDS reads),
 //    and a store of (O / l in bf16, m, l) for each row at its list position.
-//  * Combine kernel: one wave per (group, query).  Lane s holds slot s (kept as in the
-//    forward: valid, causal, first occurrence); it finds the query's list position in
-//    its block's list; the kept partials are merged four at a time:
+//  * Combine kernel: one wave per (group, query), or per 2, 4 or 8 consecutive ones when
+//    the G heads' outputs fill fewer than 33 lanes.  Lane s holds slot s (kept as in
+//    the forward: valid, causal, first occurrence) and finds the query's list position
+//    in its block's list; the kept partials are merged in slot order, their loads
+//    issued several at a time:
 //    M = max m_s, L = sum l_s 2^(m_s - M), out = sum l_s 2^(m_s - M) (O_s / l_s) / L,
 //    lse = (M + log2 L) ln 2; no kept slot gives out = 0 and lse = -1e9.
 #include <type_traits>
@@ -262,42 +264,62 @@ __global__ __launch_bounds__(64 * kFsaWaves) void nsa_fsa_partial_kernel(
     }
 }
 
-// One wave per (group, query); 8-dim pieces of the G heads' outputs spread over the lanes.
-template <int D>
+// One wave per QPW consecutive (group, query) rows; the G heads' outputs of a row are cut
+// into 8-dim pieces, spread over the row's 64 / QPW lanes (CPL pieces per lane).  Small
+// groups put several rows in a wave so that every lane merges; KPR partials are loaded
+// per round before any is merged.
+template <int D, int QPW, int CPL, int KPR>
 __global__ __launch_bounds__(256) void nsa_fsa_combine_kernel(
     const int32_t *__restrict__ IDX, const uint32_t *__restrict__ bits,
     const int32_t *__restrict__ rank, const uint16_t *__restrict__ PA,
     const float *__restrict__ PM, const float *__restrict__ PL, uint16_t *__restrict__ O,
     float *__restrict__ LSE, int Hq, int Hkv, int G, int T, int S, int nblk, int words,
     int64_t nrows) {
-    constexpr int DC = D / 8;   // 8-dim pieces per head
-    constexpr int CPL = 4;      // pieces per lane: G * DC <= 16 * 16 = 256
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= nrows) return;   // no barrier in this kernel
-    const int lane = threadIdx.x & 63;
-    const int64_t group = row / T;
-    const int i = (int)(row % T);
-    const int b = (int)(group / Hkv), kv = (int)(group % Hkv);
-
-    // kept slots (valid, not after the query's block, first occurrence), each lane its
-    // own slot's list position
-    const int32_t *slots = IDX + row * S;
-    const int myblk = lane < S ? slots[lane] : -1;
-    bool keep = myblk >= 0 && myblk < nblk && myblk * (T / nblk) <= i;
-    for (int s2 = 0; s2 < S; ++s2) {
-        const int other = __builtin_amdgcn_readlane(myblk, s2);
-        keep = keep && !(s2 < lane && other == myblk);
-    }
-    int mypos = 0;
-    if (keep) {
-        const int64_t lst = group * nblk + myblk;
-        const int w = i >> 5;
-        const uint32_t word = bits[lst * words + w];
-        mypos = rank[lst * words + w] + __builtin_popcount(word & ((1u << (i & 31)) - 1u));
-    }
-    uint64_t rem = __builtin_amdgcn_ballot_w64(keep);
-
+    constexpr int DC = D / 8;       // 8-dim pieces per head
+    constexpr int LPQ = 64 / QPW;   // lanes per row
+    static_assert(QPW == 1 || CPL == 1, "several rows per wave only with one piece per lane");
+    __shared__ int kpos[4][QPW][64];  // per wave and row: list positions of the kept slots
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * QPW;
+    if (row0 >= nrows) return;      // no barrier in this kernel
+    const int qsub = lane / LPQ, cl = lane % LPQ;
     const int nch = G * DC;
+
+    // slot pass, one row at a time, lane s holding slot s: kept slots (valid, not after
+    // the query's block, first occurrence) leave their list positions in slot order
+    int nk_mine = 0, maxnk = 0;
+#pragma unroll
+    for (int r = 0; r < QPW; ++r) {
+        const int64_t row = row0 + r;
+        if (row >= nrows) break;
+        const int64_t group = row / T;
+        const int i = (int)(row % T);
+        const int32_t *slots = IDX + row * S;
+        const int myblk = lane < S ? slots[lane] : -1;
+        bool keep = myblk >= 0 && myblk < nblk && myblk * (T / nblk) <= i;
+        for (int s2 = 0; s2 < S; ++s2) {
+            const int other = __builtin_amdgcn_readlane(myblk, s2);
+            keep = keep && !(s2 < lane && other == myblk);
+        }
+        const uint64_t kept = __builtin_amdgcn_ballot_w64(keep);
+        if (keep) {
+            const int64_t lst = group * nblk + myblk;
+            const int w = i >> 5;
+            const uint32_t word = bits[lst * words + w];
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(kept >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)kept, 0u));
+            kpos[wave][r][below] =
+                rank[lst * words + w] + __builtin_popcount(word & ((1u << (i & 31)) - 1u));
+        }
+        const int n = __builtin_popcountll(kept);
+        if (qsub == r) nk_mine = n;
+        maxnk = max(maxnk, n);
+    }
+    // the positions were written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
     float M[CPL], L[CPL], acc[CPL][8];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -306,31 +328,21 @@ __global__ __launch_bounds__(256) void nsa_fsa_combine_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
     }
-    while (rem) {
-        // up to four kept slots per round: all their loads first, then the merges
-        int ps[4];
-        int nk = 0;
+    for (int base = 0; base < maxnk; base += KPR) {
+        int ps[KPR];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            ps[t] = -1;
-            if (rem) {
-                const int s = __builtin_ctzll(rem);
-                rem &= rem - 1;
-                ps[t] = __builtin_amdgcn_readlane(mypos, s);
-                ++nk;
-            }
-        }
-        float pm[4][CPL], pl[4][CPL];
-        bf16x8 pa[4][CPL];
+        for (int t = 0; t < KPR; ++t) ps[t] = base + t < nk_mine ? kpos[wave][qsub][base + t] : -1;
+        float pm[KPR][CPL], pl[KPR][CPL];
+        bf16x8 pa[KPR][CPL];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < KPR; ++t)
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int c = lane + 64 * j;
+                const int c = cl + LPQ * j;
                 pm[t][j] = -INFINITY;
                 pl[t][j] = 0.0f;
                 pa[t][j] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-                if (t < nk && c < nch) {
+                if (ps[t] >= 0 && c < nch) {
                     const size_t pr = (size_t)ps[t] * G + c / DC;
                     pm[t][j] = PM[pr];
                     pl[t][j] = PL[pr];
@@ -338,8 +350,8 @@ __global__ __launch_bounds__(256) void nsa_fsa_combine_kernel(
                 }
             }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t >= nk) break;
+        for (int t = 0; t < KPR; ++t) {
+            if (ps[t] < 0) continue;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const float mn = fmaxf(M[j], pm[t][j]);
@@ -352,9 +364,14 @@ __global__ __launch_bounds__(256) void nsa_fsa_combine_kernel(
             }
         }
     }
+    const int64_t row = row0 + qsub;
+    if (row >= nrows) return;
+    const int64_t group = row / T;
+    const int i = (int)(row % T);
+    const int b = (int)(group / Hkv), kv = (int)(group % Hkv);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int c = lane + 64 * j;
+        const int c = cl + LPQ * j;
         if (c >= nch) continue;
         const int h = kv * G + c / DC;
         const size_t orow = ((size_t)b * Hq + h) * T + i;
@@ -367,6 +384,26 @@ __global__ __launch_bounds__(256) void nsa_fsa_combine_kernel(
         if (LSE != nullptr && c % DC == 0)
             LSE[orow] = L[j] > 0.0f ? (M[j] + __builtin_amdgcn_logf(L[j])) * kLn2 : -1e9f;
     }
+}
+
+// Rows per wave and pieces per lane for G heads of D dims: nch = G * D / 8 pieces per
+// row; up to 32 pieces put 64 / nch (rounded down to a power of two) rows in a wave.
+template <int D, int QPW, int CPL, int KPR>
+hipError_t launch_combine(void **args, int64_t nrows, hipStream_t stream) {
+    const int64_t waves = (nrows + QPW - 1) / QPW;
+    return hipLaunchKernel((const void *)nsa_fsa_combine_kernel<D, QPW, CPL, KPR>,
+                           dim3((unsigned)((waves + 3) / 4)), dim3(256), args, 0, stream);
+}
+
+template <int D>
+hipError_t combine(void **args, int G, int64_t nrows, hipStream_t stream) {
+    const int nch = G * (D / 8);
+    if (nch <= 8) return launch_combine<D, 8, 1, 8>(args, nrows, stream);
+    if (nch <= 16) return launch_combine<D, 4, 1, 8>(args, nrows, stream);
+    if (nch <= 32) return launch_combine<D, 2, 1, 8>(args, nrows, stream);
+    if (nch <= 64) return launch_combine<D, 1, 1, 8>(args, nrows, stream);
+    if (nch <= 128) return launch_combine<D, 1, 2, 8>(args, nrows, stream);
+    return launch_combine<D, 1, 4, 4>(args, nrows, stream);
 }
 
 // Workspace: the inverted index, then the partials: O / l bf16 [pairs][G][D], m and l
@@ -425,8 +462,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
         int64_t nrows = (int64_t)B * Hkv * T;
         void *a[] = {&idx, &bits, &rank, &pa, &pm, &pl, &out, &lse, &Hq, &Hkv, &G, &T, &S,
                      &nblk, &words, &nrows};
-        return hipLaunchKernel((const void *)nsa_fsa_combine_kernel<D>,
-                               dim3((unsigned)((nrows + 3) / 4)), dim3(256), a, 0, stream);
+        return combine<D>(a, G, nrows, stream);
     }
 }
 

@@ -1,8 +1,9 @@
 """GPU parity of the block-outer NSA selection forward (nsa_sel_fwd_fsa) against the
 fp64 oracle: the query-outer forward's small shapes and block_idx edge cases, lists
 long enough to be split over several workgroups, dense equivalence, exact token
-counts with q = 0, set semantics, determinism, workspace reuse, and the T=4096 G=8 and
-T=32768 G=16 configurations on sampled rows."""
+counts with q = 0, set semantics, determinism, workspace reuse, T=8192 with the small
+groups (G = 1 and 4) where this form is the faster one, and the T=4096 G=8 and T=32768
+G=16 configurations."""
 import math
 
 import numpy as np
@@ -150,3 +151,18 @@ def test_fsa_config_T32768_G16(gpu, nsa_c5_case):
     assert_rows_close(o.reshape(-1, D)[c["rows"]], c["ref_o"], BF16_REL, "fsa T32768 G16")
     assert_lse_close(lse.reshape(-1)[c["rows"]], c["ref_lse"], "fsa T32768 G16")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("Hkv", [16, 4], ids=["G1", "G4"])
+def test_fsa_small_groups_T8192(gpu, Hkv):
+    """B=1 Hq=16 T=8192 D=128 bs=64 S=16 with G = 1 and G = 4 (block lists as in the
+    benchmarked configurations): every element of o and lse against the oracle."""
+    B, Hq, T, D, bs, S = 1, 16, 8192, 128, 64, 16
+    print(f"fsa T8192 Hkv={Hkv}: inputs", flush=True)
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=Hkv)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=Hkv)
+    o, lse = _run(q, k, v, idx, bs, gpu)
+    print(f"fsa T8192 Hkv={Hkv}: oracle", flush=True)
+    ro, rl = oracle.nsa_ref(q, k, v, idx, bs)
+    assert_rows_close(o, ro, BF16_REL, f"fsa T8192 G{Hq // Hkv}")
+    assert_lse_close(lse, rl, f"fsa T8192 G{Hq // Hkv}")
