@@ -14,7 +14,8 @@
 // Kernels (all on the caller's stream, workspace from the caller):
 //  * The selection inverted (nsa_index.hip): for each (group, block) the increasing
 //    list of queries that attend it, cut into segments of at most kNsaSegQ queries.
-//  * dq: one wavefront per (group, query), as the forward: the G heads fill the N
+//  * dq: one wavefront per (group, query), as the forward (kept blocks walked in
+//    decreasing block order): the G heads fill the N
 //    dimension of 16x16x32 MFMAs, S^T = K Q^T and dP^T = V dO^T per 32-key chunk,
 //    P = exp2(S' - lse') from the forward's lse, dS^T rounded to bf16 in register
 //    order, and dQ^T += K^T (.)^T.  K and V rows go by DMA, whole rows per
@@ -120,7 +121,17 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
         const int other = __builtin_amdgcn_readlane(myblk, s2);
         keep = keep && !(s2 < lane && other == myblk);
     }
-    uint64_t rem = __builtin_amdgcn_ballot_w64(keep);
+    // The kept blocks are visited in decreasing block order, as in the forward (lane s's
+    // rank = the number of kept blocks above its own): the waves of neighbouring queries
+    // then read nearby blocks at the same time, which keeps more of them in L2.
+    const uint64_t kept = __builtin_amdgcn_ballot_w64(keep);
+    const int nkept = __builtin_popcountll(kept);
+    int rank = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+        const int other = __builtin_amdgcn_readlane(myblk, s2);
+        rank += (int)(((kept >> s2) & 1) != 0 && other > myblk);
+    }
+    int taken = 0;
 
     // Q^T and dO^T operands: head kv*G + n16 (zero for n16 >= G), dims 32*ds + 8*g4 .. +7
     const bool head_ok = n16 < G;
@@ -223,9 +234,9 @@ __global__ __launch_bounds__(64 * kDqWaves) void nsa_bwd_dq_kernel(
             ++cur_c;
             return cur_blk * BS + cur_c * kChunk;
         }
-        if (rem == 0) return -1;
-        const int s = __builtin_ctzll(rem);
-        rem &= rem - 1;
+        if (taken == nkept) return -1;
+        const int s = __builtin_ctzll(__builtin_amdgcn_ballot_w64(keep && rank == taken));
+        ++taken;
         cur_blk = __builtin_amdgcn_readlane(myblk, s);
         cur_c = 0;
         return cur_blk * BS;

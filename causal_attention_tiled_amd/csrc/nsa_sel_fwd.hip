@@ -237,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void nsa_sel_fwd_kernel(
     using vdma_ops = std::integral_constant<int, VDMA>;
     using no_ops = std::integral_constant<int, 0>;
 
-    // Walk the chunks of the kept blocks in slot order: chunk (blk, c) starts at key
+    // Walk the chunks of the kept blocks in decreasing block order: chunk (blk, c) starts at key
     // blk*BS + 32*c and exists while it starts at or before i.
     int cur_blk = -1, cur_c = 0;
     auto next_chunk = [&]() -> int {

@@ -11,6 +11,8 @@ attention library's C ABI).
 ``mfma_chain_rate(chains)``  bf16 MFMA TFLOP/s of one wave per SIMD running 1, 2 or 4
                             independent chains of dependent MFMAs.
 ``transcendental_rate()``   v_log_f32 + v_exp_f32 instructions per second (lane ops).
+``lds_rate(mode)``          LDS read bytes per shader clock per compute unit, and TB/s over
+                            the chip, of ds_read_b128 (mode 0) or ds_read_b64_tr_b16 (1).
 """
 from __future__ import annotations
 
@@ -35,6 +37,8 @@ def _load():
         lib.probe_trans.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
         lib.probe_mfma_chains.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
         lib.probe_mfma_chains.restype = ctypes.c_int
+        lib.probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+        lib.probe_lds.restype = ctypes.c_int
         for f in (lib.probe_read, lib.probe_mfma, lib.probe_trans):
             f.restype = ctypes.c_int
         _lib = lib
@@ -129,3 +133,26 @@ def transcendental_rate(iters: int = 4000, reps: int = 3) -> float:
             raise RuntimeError(f"probe_trans failed: {rc}")
     ms = _time_ms(launch, reps)
     return 2.0 * 8 * iters * 256 * grid / (ms * 1e-3)
+
+
+def lds_rate(mode: int, iters: int = 20000, reps: int = 3):
+    """(bytes per shader clock per compute unit, TB/s over the chip) of LDS reads: 4
+    workgroups of 4 waves per compute unit, 8 reads per wave per iteration (mode 0:
+    ds_read_b128, 1 KiB per read; mode 1: ds_read_b64_tr_b16, 512 bytes)."""
+    import torch
+    lib = _load()
+    grid = 4 * _CUS
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    clk = torch.zeros(2 * 4 * grid, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        rc = lib.probe_lds(iters, mode, grid, sink.data_ptr(), clk.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_lds failed: {rc}")
+    ms = _time_ms(launch, reps)
+    per_read = 1024 if mode == 0 else 512
+    total = float(per_read) * 8 * iters * 4 * grid
+    c = clk.view(-1, 2).double()
+    cycles = float(c[:, 0].median())
+    return total / _CUS / cycles, total / (ms * 1e-3) / 1e12

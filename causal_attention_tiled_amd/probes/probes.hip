@@ -11,7 +11,10 @@
 //  * mfma_chain_kernel: one wave per SIMD running 1, 2 or 4 independent chains of
 //    dependent MFMAs, to measure how fast a dependent MFMA issues behind its predecessor;
 //  * trans_kernel: independent chains of v_log_f32 followed by v_exp_f32 (the pair the
-//    general-power epilogue x^p = exp2(p log2 x) issues per element).
+//    general-power epilogue x^p = exp2(p log2 x) issues per element);
+//  * lds_kernel: LDS read throughput of ds_read_b128 (16 bytes per lane) or of the
+//    transposing ds_read_b64_tr_b16 (8 bytes per lane), bank-conflict-free addresses,
+//    timed by the shader clock on each wave.
 // Every loop is bounded by its arguments and every access stays inside its buffer.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -130,6 +133,47 @@ __global__ __launch_bounds__(256) void trans_kernel(int iters, float *__restrict
     if (s == 1234.5f) sink[0] = s;
 }
 
+// Each workgroup fills a 32 KiB LDS buffer, then each wave reads it `iters` times 8
+// reads per iteration: MODE 0 ds_read_b128 with lane l at 16-byte chunk (l + 64 j + 512 s)
+// mod 2048 (16 consecutive lanes cover the 64 banks once), MODE 1 ds_read_b64_tr_b16 with
+// lane l at 8-byte chunk (l + 64 j + 512 s) mod 4096.  clk as in mfma_kernel.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+template <int MODE>
+__global__ __launch_bounds__(256) void lds_kernel(int iters, uint32_t *__restrict__ sink,
+                                                  uint64_t *__restrict__ clk) {
+    __shared__ __attribute__((aligned(16))) u32x4 buf[2048];
+    for (int k = threadIdx.x; k < 2048; k += 256)
+        buf[k] = u32x4{(uint32_t)k, (uint32_t)k * 3u, (uint32_t)k * 5u, (uint32_t)k * 7u};
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    for (int i = 0; i < iters; ++i) {
+        const int s = 512 * (i & 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (MODE == 0) {
+                acc ^= buf[(lane + 64 * j + s) & 2047];
+            } else {
+                const int c = (lane + 64 * j + s) & 4095;
+                const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4i16 *)((__attribute__((address_space(3))) uint8_t *)buf + 8 * c));
+                acc[j & 3] ^= (uint32_t)(uint16_t)v[0] | ((uint32_t)(uint16_t)v[1] << 16);
+                acc[(j + 1) & 3] ^= (uint32_t)(uint16_t)v[2] | ((uint32_t)(uint16_t)v[3] << 16);
+            }
+        }
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == kNever) sink[0] = acc[0];
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (lane == 0) {
+        clk[2 * w] = t1 - t0;
+        clk[2 * w + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 // Streaming read of `bytes` (a multiple of 128) at `buf`, `passes` times, by `grid`
@@ -172,5 +216,19 @@ PROBE_EXPORT int probe_trans(int iters, int grid, void *sink, void *stream) {
     if (!sink || iters < 1 || grid < 1) return -1;
     hipLaunchKernelGGL(trans_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
                        (float *)sink);
+    return (int)hipGetLastError();
+}
+
+// `iters` iterations of 8 LDS reads per wave (mode 0: ds_read_b128, 1 KiB per read and
+// wave; mode 1: ds_read_b64_tr_b16, 512 bytes), `grid` workgroups of 4 waves; clk holds
+// 2 uint64 per wave (shader cycles, 100 MHz ticks).
+PROBE_EXPORT int probe_lds(int iters, int mode, int grid, void *sink, void *clk, void *stream) {
+    if (!sink || !clk || iters < 1 || grid < 1 || (mode != 0 && mode != 1)) return -1;
+    if (mode == 0)
+        hipLaunchKernelGGL(lds_kernel<0>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
+                           (uint32_t *)sink, (uint64_t *)clk);
+    else
+        hipLaunchKernelGGL(lds_kernel<1>, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
+                           (uint32_t *)sink, (uint64_t *)clk);
     return (int)hipGetLastError();
 }

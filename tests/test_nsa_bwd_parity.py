@@ -117,6 +117,27 @@ def test_nsa_bwd_deterministic(gpu):
         assert torch.equal(x, y)
 
 
+def test_nsa_bwd_slot_set_semantics(gpu):
+    """The selection is a set: repeating or permuting the slots leaves dq, dk and dv
+    unchanged bit for bit (dq visits the kept blocks in decreasing block order, dk/dv
+    walk the inverted lists), and the result matches the oracle."""
+    B, Hq, Hkv, T, D, bs, S = 1, 8, 2, 512, 128, 64, 5
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=9)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=9)
+    do = _dout((B, Hq, T, D), seed=10)
+    a = _run(q, k, v, idx, bs, do, gpu)
+    dup = np.concatenate([idx, idx[..., :3]], axis=-1)
+    perm = np.argsort(np.random.default_rng(1).random(dup.shape), axis=-1)
+    b = _run(q, k, v, np.ascontiguousarray(np.take_along_axis(dup, perm, axis=-1)), bs, do, gpu)
+    for name, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), f"{name} depends on the slot order"
+    ref = oracle.nsa_bwd_ref(q, k, v, idx, bs, do)
+    assert_rows_close(a[0], ref[0], BF16_REL, "dq set", floor=FLOOR,
+                      floor_rows=_single_key_rows(idx, bs, Hq // Hkv))
+    assert_rows_close(a[1], ref[1], BF16_REL, "dk set")
+    assert_rows_close(a[2], ref[2], BF16_REL, "dv set")
+
+
 @pytest.mark.parametrize("name", ["nsa_bf16_T4096_G8", "nsa_bf16_T32768_G16"])
 def test_nsa_bwd_config_sampled(gpu, name):
     c = inputs.CONFIGS[name]
