@@ -51,9 +51,7 @@ constexpr int tra_bf16_rows(int D) { return 32 * tra_bf16_waves(D); }
 constexpr int kTraF32Rows = 16;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;
-// Query rows (dq kernel) and key rows (dk/dv kernel) per workgroup of the
-// Threshold Rectified Attention backward.
-constexpr int kTraBwdDqRows = 128;
+// Key rows per workgroup of the Threshold Rectified Attention backward's dk/dv kernel.
 constexpr int kTraBwdDkvRows = 128;
 
 // Host-side launchers (one per kernel family); they pick the template

@@ -10,12 +10,14 @@
 //
 // Two kernels, as on the page, so that every gradient row is written by exactly
 // one wavefront (no atomics; the result does not depend on scheduling):
-//  * tra_bwd_dq_kernel: the forward's layout with 128 query rows per workgroup (4
-//    wavefronts of 32 rows, one per SIMD: the Q and dO operands, the dQ
-//    accumulator and three operand streams need more than half of a SIMD's
-//    registers), transposed score tiles so tau and the mask are per lane.  Per 32-key block: S^T = K Q^T, dP^T = V dO^T, then
-//    A^T = dP^T * g (rounded to bf16, in the accumulator's register order) and
-//    dQ^T += K^T A^T with K^T read transposed from LDS.  K and V tiles stream
+//  * tra_bwd_dq_kernel: the forward's layout, 32 query rows per wavefront, 8
+//    wavefronts (256 rows, two per SIMD) per workgroup at D = 128 and 4 at D = 64,
+//    transposed score tiles so tau and the mask are per lane.  Per 32-key block:
+//    S^T = K Q^T, dP^T = V dO^T, then A^T = dP^T * g (rounded to bf16, in the
+//    accumulator's register order) and dQ^T += K^T A^T with K^T read transposed
+//    from LDS, each operand read just before its product so that the Q and dO
+//    operands and the dQ accumulator leave room for two waves per SIMD; the
+//    other wave of the SIMD covers the read latency.  K and V tiles stream
 //    HBM -> LDS by DMA, double-buffered, as in the forward.
 //  * tra_bwd_dkv_kernel: 128 key rows per workgroup, 4 wavefronts of 32 keys, one
 //    per SIMD (the dK and dV accumulators take 128 registers per lane).  A wave
@@ -32,8 +34,10 @@
 namespace attn {
 namespace {
 
-constexpr int kDqWaves = 4;   // dq kernel: 32 query rows per wave, one wave per SIMD
-static_assert(kDqWaves * 32 == kTraBwdDqRows, "dq workgroup rows");
+// dq kernel waves per workgroup (32 query rows each): at D = 128 eight, two per SIMD
+// (256 registers each); at D = 64 four, with two or three workgroups per compute unit
+template <int D>
+constexpr int dq_waves() { return D == 128 ? 8 : 4; }
 constexpr int kDkvWaves = 4;  // dk/dv kernel: 32 key rows per wave
 static_assert(kDkvWaves * 32 == kTraBwdDkvRows, "dk/dv workgroup rows");
 constexpr int kBN = 64;       // keys (dq kernel) or queries (dk/dv kernel) per LDS tile
@@ -64,7 +68,7 @@ __device__ __forceinline__ void key_tile_order(int bid, int BH, int nkt, int &bh
     }
 }
 
-template <int D, int PM>
+template <int D, int PM, int kDqWaves = dq_waves<D>()>
 __global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dQ,
@@ -164,9 +168,6 @@ __global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
         }
     }
     const float tau = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
-    f32x16 zero16;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
 
@@ -181,11 +182,8 @@ __global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    // Per 32-key block, four phases:
-    //   1: S^T = K Q^T                          (V operand read alongside)
-    //   2: dP^T = V dO^T || S^T <- max(S^T - tau, 0)^(p-1)
-    //   3: A^T = bf16(dP^T * S^T)                (K^T operand read alongside)
-    //   4: dQ^T += K^T A^T                       (next block's K operand read alongside)
+    // Per 32-key block: S^T = K Q^T, dP^T = V dO^T, S^T <- max(S^T - tau, 0)^(p-1),
+    // A^T = bf16(dP^T * S^T), dQ^T += K^T A^T.
     auto tile = [&](int n, auto masked, int buf) {
         constexpr bool kMasked = decltype(masked)::value;
         if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
@@ -195,60 +193,24 @@ __global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
                 return;
             }
         }
-        bf16x8 kf[NDS], vf[NDS], ktf[NDT][2], af[2];
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) kf[ds] = row_frag(KB, buf, 0, ds);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s = zero16, dp = zero16;
-            // 1
+            f32x16 s = {}, dp = {};
+            bf16x8 af[2];
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) vf[ds] = row_frag(VB, buf, kb, ds);
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(kf[ds], qf[ds], s);
-#pragma unroll
-            for (int i = 0; i < NDS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(row_frag(KB, buf, kb, ds), qf[ds], s);
             if constexpr (kMasked) mask_block(s, n * kBN + 32 * kb);
-            // 2
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(vf[ds], df[ds], dp);
+            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(row_frag(VB, buf, kb, ds), df[ds], dp);
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = relu_pow_m1<PM>(s[r] - tau, p);
 #pragma unroll
-            for (int i = 0; i < NDS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // 3
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) ktf[dt][c] = kt_frag(buf, kb, dt, c);
-#pragma unroll
             for (int r = 0; r < 16; ++r) af[r >> 3][r & 7] = (__bf16)(dp[r] * s[r]);
-            __builtin_amdgcn_sched_barrier(0);
-            // 4
-            if (kb == 0) {
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) kf[ds] = row_frag(KB, buf, 1, ds);
-            }
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) dqacc[dt] = mfma_32x32x16(ktf[dt][c], af[c], dqacc[dt]);
-            if (kb == 0) {
-#pragma unroll
-                for (int i = 0; i < 2 * NDT; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int dt = 0; dt < NDT; ++dt)
+                    dqacc[dt] = mfma_32x32x16(kt_frag(buf, kb, dt, c), af[c], dqacc[dt]);
         }
         tile_sync();
     };
@@ -541,10 +503,11 @@ template <int D, int PM>
 hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
                   uint16_t *dq, uint16_t *dk, uint16_t *dv, int BH, int T, float beta, float p,
                   hipStream_t stream) {
-    int nqt = (T + kTraBwdDqRows - 1) / kTraBwdDqRows;
+    constexpr int W = dq_waves<D>();
+    int nqt = (T + 32 * W - 1) / (32 * W);
     void *a1[] = {&q, &k, &v, &dout, &dq, &BH, &T, &nqt, &beta, &p};
     hipError_t e = hipLaunchKernel((const void *)tra_bwd_dq_kernel<D, PM>,
-                                   dim3((unsigned)(BH * nqt)), dim3(64 * kDqWaves), a1, 0, stream);
+                                   dim3((unsigned)(BH * nqt)), dim3(64 * W), a1, 0, stream);
     if (e != hipSuccess) return e;
     int nkt = (T + kTraBwdDkvRows - 1) / kTraBwdDkvRows;
     void *a2[] = {&q, &k, &v, &dout, &dk, &dv, &BH, &T, &nkt, &beta, &p};
