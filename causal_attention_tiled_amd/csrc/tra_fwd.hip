@@ -26,6 +26,10 @@
 //  * The wave issuing the second score block and the first epilogue runs at raised
 //    issue priority, so that of two waves on a SIMD the one with the mixed MFMA and
 //    VALU phase goes first.
+//  * For the general power at D = 64 the phases are dropped: each 32-key block runs
+//    scores, weights and P V in order and the compiler interleaves them, since the
+//    weights (a log and an exp each) are more vector work than the phase pattern
+//    leaves room for.
 //  * Launch order: the heaviest query tiles (largest i) first, and the heads split
 //    into 8 contiguous groups so that each XCD (dispatch is round-robin over the 8
 //    XCDs) works on its own heads and keeps their K/V in its private L2.
@@ -52,6 +56,7 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     constexpr int LOADS = kBN * CH / (64 * NW); // 16-byte chunks per thread per tensor
     constexpr int NDS = D / 16;                 // S^T MFMA k-steps
     constexpr int NDT = D / 32;                 // 32-dim output tiles
+    constexpr bool kPlainOrder = D == 64 && PM == kPowGeneral;  // see the tile body
     static_assert(LOADS >= 1 && kBN * CH % (64 * NW) == 0, "tile staging");
     static_assert(TILEB == NW * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
 
@@ -199,6 +204,45 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     //   D: O += V1 P1
     auto tile = [&](int n, auto masked, const TileBuf &buf, TileBuf &next) {
         constexpr bool kMasked = decltype(masked)::value;
+        if constexpr (kPlainOrder) {
+            // general power at D = 64: the weights cost a log and an exp each, more
+            // vector work than the phase interleave below leaves room for; each 32-key
+            // block is done in order and the compiler interleaves freely
+            if (n + 1 < ntiles) gload(n + 1, next);
+            if constexpr (kMasked) {
+                if (n * kBN > qw0 + 32 * QB - 1) {
+                    tile_sync();
+                    return;
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x16 sv[QB];
+                bf16x8 pf[QB][2];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sv[qb] = cinit[qb];
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) {
+                    const bf16x8 kf = k_frag(buf, kb, ds);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) sv[qb] = mfma_32x32x16(kf, qf[qb][ds], sv[qb]);
+                }
+                if constexpr (kMasked) mask_block(sv, n * kBN + 32 * kb);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) epilogue(sv[qb], pf[qb]);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const bf16x8 vfr = v_frag(buf, kb, dt, c);
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb)
+                            oacc[qb][dt] = mfma_32x32x16(vfr, pf[qb][c], oacc[qb][dt]);
+                    }
+            }
+            tile_sync();
+            return;
+        }
         bf16x8 ka[NDS], kb1[NDS], va[NDT][2], vb[NDT][2];
         f32x16 s0[QB], s1[QB];
         bf16x8 p0[QB][2], p1[QB][2];
