@@ -215,9 +215,6 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
         qnorm(qf2);
     }
     const float tau = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
-    f32x16 zero16;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zero16[r] = 0.0f;
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
@@ -233,14 +230,10 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
         __builtin_amdgcn_s_barrier();
     };
 
-    // Per 32-key block, four phases (each wave's VALU-only stretch is covered by
-    // the MFMAs of the other wave on its SIMD):
-    //   1: S1 = K1 Q1^T                       (K2 operand read alongside)
-    //   2: S2 = K2 Q2^T || S1 <- relu(S1 - tau)^p
-    //   3: P = bf16(S1 - lam * relu(S2 - tau)^p)  (V operand read alongside)
-    //   4: O += V P                            (next block's K1 operand read alongside)
-    // Phase 2 runs at raised issue priority: of two waves on a SIMD, the one in the
-    // mixed MFMA + VALU phase goes first.
+    // Per 32-key block, in order: S1 = K1 Q1^T, S2 = K2 Q2^T, the mask,
+    // P = bf16(relu(S1 - tau)^p - lam * relu(S2 - tau)^p), O += V P; each operand is
+    // read from LDS just before its product and the compiler interleaves the rest
+    // (the other wave on the SIMD covers each wave's vector-only stretch).
     auto tile = [&](int n, auto masked, int buf) {
         constexpr bool kMasked = decltype(masked)::value;
         if (n + 1 < ntiles) gload(n + 1, buf ^ 1);
@@ -251,71 +244,32 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
                 return;
             }
         }
-        bf16x8 k1f[NDS], k2f[NDS], vf[NDT][2], pf[2];
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) k1f[ds] = k_frag(K1B, buf, 0, ds);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s1 = zero16, s2 = zero16;
-            // 1
+            f32x16 s1 = {}, s2 = {};
+            bf16x8 pf[2];
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) k2f[ds] = k_frag(K2B, buf, kb, ds);
+            for (int ds = 0; ds < NDS; ++ds) s1 = mfma_32x32x16(k_frag(K1B, buf, kb, ds), qf1[ds], s1);
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s1 = mfma_32x32x16(k1f[ds], qf1[ds], s1);
-#pragma unroll
-            for (int i = 0; i < NDS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int ds = 0; ds < NDS; ++ds) s2 = mfma_32x32x16(k_frag(K2B, buf, kb, ds), qf2[ds], s2);
+            if constexpr (kMasked) {
+                mask_block(s1, n * kBN + 32 * kb);
+                mask_block(s2, n * kBN + 32 * kb);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kMasked) mask_block(s1, n * kBN + 32 * kb);
-            // 2 (raised issue priority until 3)
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s2 = mfma_32x32x16(k2f[ds], qf2[ds], s2);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s1[r] = relu_pow<PM>(s1[r] - tau, p);
-#pragma unroll
-            for (int i = 0; i < NDS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kMasked) mask_block(s2, n * kBN + 32 * kb);
-            // 3
-            __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) vf[dt][c] = v_frag(buf, kb, dt, c);
             {
-                // relu(s2)^p rounded on its own, then one fused multiply-add: with
-                // identical paths and lam = 1 the two weights cancel exactly
 #pragma clang fp contract(off)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    const float w1 = relu_pow<PM>(s1[r] - tau, p);
                     const float w2 = relu_pow<PM>(s2[r] - tau, p);
-                    pf[r >> 3][r & 7] = (__bf16)__builtin_fmaf(-lam, w2, s1[r]);
+                    pf[r >> 3][r & 7] = (__bf16)__builtin_fmaf(-lam, w2, w1);
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // 4
-            if (kb == 0) {
-#pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) k1f[ds] = k_frag(K1B, buf, 1, ds);
             }
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma_32x32x16(vf[dt][c], pf[c], oacc[dt]);
-            if (kb == 0) {
-#pragma unroll
-                for (int i = 0; i < 2 * NDT; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int dt = 0; dt < NDT; ++dt)
+                    oacc[dt] = mfma_32x32x16(v_frag(buf, kb, dt, c), pf[c], oacc[dt]);
         }
         tile_sync();
     };
