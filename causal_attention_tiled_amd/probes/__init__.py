@@ -11,8 +11,8 @@ attention library's C ABI).
 ``mfma_chain_rate(chains)``  bf16 MFMA TFLOP/s of one wave per SIMD running 1, 2 or 4
                             independent chains of dependent MFMAs.
 ``transcendental_rate()``   v_log_f32 + v_exp_f32 instructions per second (lane ops).
-``lds_rate(mode)``          LDS read bytes per shader clock per compute unit, and TB/s over
-                            the chip, of ds_read_b128 (mode 0) or ds_read_b64_tr_b16 (1).
+``lds_rate(mode)``          LDS read TB/s over the chip, and bytes per shader clock per
+                            compute unit, of ds_read_b128 (mode 0) or ds_read_b64_tr_b16 (1).
 """
 from __future__ import annotations
 
@@ -136,9 +136,10 @@ def transcendental_rate(iters: int = 4000, reps: int = 3) -> float:
 
 
 def lds_rate(mode: int, iters: int = 20000, reps: int = 3):
-    """(bytes per shader clock per compute unit, TB/s over the chip) of LDS reads: 4
+    """(TB/s over the chip, bytes per shader clock per compute unit) of LDS reads: 4
     workgroups of 4 waves per compute unit, 8 reads per wave per iteration (mode 0:
-    ds_read_b128, 1 KiB per read; mode 1: ds_read_b64_tr_b16, 512 bytes)."""
+    ds_read_b128, 1 KiB per read; mode 1: ds_read_b64_tr_b16, 512 bytes).  The clock is
+    the median over waves of shader cycles over 100 MHz ticks during the loop."""
     import torch
     lib = _load()
     grid = 4 * _CUS
@@ -154,5 +155,6 @@ def lds_rate(mode: int, iters: int = 20000, reps: int = 3):
     per_read = 1024 if mode == 0 else 512
     total = float(per_read) * 8 * iters * 4 * grid
     c = clk.view(-1, 2).double()
-    cycles = float(c[:, 0].median())
-    return total / _CUS / cycles, total / (ms * 1e-3) / 1e12
+    ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
+    tbps = total / (ms * 1e-3) / 1e12
+    return tbps, tbps * 1e12 / _CUS / (ghz * 1e9)

@@ -296,7 +296,8 @@ size_t nsa_sel_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, int blo
  * group, query), this form once per (kv group, block segment) but writes and
  * reads a partial per (query, block, head).  Measured on MI355X at Hq=16,
  * T=8192, D=128, block 64, S=16: this form is faster for G = Hq/Hkv <= 4
- * (2.2x at G=1, 1.7x at G=2, 1.3x at G=4), nsa_sel_fwd for G >= 8.
+ * (about 5.5x at G=1, 3x at G=2, 1.6x at G=4), nsa_sel_fwd for G >= 8
+ * (0.8x at G=8, 0.4x at G=16).
  */
 int nsa_sel_fwd_fsa(const void *q, const void *k, const void *v, const int32_t *block_idx,
                     void *out, float *lse, void *workspace, size_t workspace_bytes,
