@@ -176,6 +176,25 @@ def cpu_baseline_nsa(qn, kn, vn, idx_np, budget_s=8.0):
                       f"({spent:.1f} s), fp64; bytes counted per head"}
 
 
+def cpu_full(q, k, v, qn, kn, vn, idx_np):
+    """The fp64 oracle over every row of both headline workloads, each in one timed call
+    (wall clock): tra_fwd B2 H32 T8192 D128 p2 and nsa_sel_fwd B1 Hq64 Hkv4 T32768 G16."""
+    import oracle
+    out = {"cores": oracle.num_threads(), "kind": "oracle"}
+    t0 = time.perf_counter()
+    oracle.tra_ref(q, k, v, TRA["beta"], TRA["p"])
+    s = time.perf_counter() - t0
+    fl = tra_useful_flops(TRA["B"], TRA["H"], TRA["T"], TRA["D"])
+    out["tra_fwd"] = {"s": s, "tflops": fl / s / 1e12, "rows": TRA["B"] * TRA["H"] * TRA["T"]}
+    t0 = time.perf_counter()
+    oracle.nsa_ref(qn, kn, vn, idx_np, NSA["block_size"])
+    s = time.perf_counter() - t0
+    gb = nsa_gathered_bytes(idx_np, NSA["T"], NSA["block_size"], NSA["D"])
+    out["nsa_sel_fwd"] = {"s": s, "gathered_gbps": gb / s / 1e9,
+                          "rows": NSA["B"] * NSA["Hq"] * NSA["T"]}
+    return out
+
+
 def time_launches(fn, warm, timed, between=None):
     """Per-launch durations (ms) of fn() from HIP events on the current stream;
     between() (not timed) runs before every launch when given."""
@@ -376,6 +395,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also time the oracle over every row of both headline workloads "
+                         "(about a minute of host time)")
     ap.add_argument("--only", choices=["tra", "nsa"], default=None,
                     help="launch only one of the two forwards (for profiling runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -546,6 +568,9 @@ def main():
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(q, k, v, idx_np)
         result["cpu_baseline_nsa"] = cpu_baseline_nsa(qn, kn, vn, idx_np)
+    if args.cpu_full:
+        print("bench: oracle over the full workloads", file=sys.stderr, flush=True)
+        result["cpu_full"] = cpu_full(q, k, v, qn, kn, vn, idx_np)
     print(json.dumps(result), flush=True)
 
 

@@ -142,8 +142,8 @@ def test_fsa_matches_query_outer_T4096_G8(gpu, nsa_c4_case):
 
 
 def test_fsa_config_T32768_G16(gpu, nsa_c5_case):
-    """B=1 Hq=64 Hkv=4 T=32768 D=128 bs=64 S=16: every head at every fourth query
-    position, the first 64 positions and the last one against the oracle."""
+    """B=1 Hq=64 Hkv=4 T=32768 D=128 bs=64 S=16: every element of o and lse against the
+    oracle."""
     c = nsa_c5_case
     print("fsa T32768: gpu", flush=True)
     o, lse = _run(c["q"], c["k"], c["v"], c["idx"], c["c"]["block_size"], gpu)
