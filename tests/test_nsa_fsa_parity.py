@@ -28,9 +28,12 @@ def _run(q, k, v, idx, bs, dev, want_lse=True, workspace=None):
     return o.cpu(), (lse.cpu() if lse is not None else None)
 
 
-# the last two select every causal block: early blocks have lists of more than 512
-# queries, processed by several workgroups
-FSA_SMALL = SMALL + [(1, 4, 1, 1056, 64, 32, 33), (1, 8, 2, 1280, 128, 64, 20)]
+# the next two select every causal block: early blocks have lists of more than 512
+# queries, processed by several workgroups; the last two cover the combine kernel's
+# remaining layouts (D = 64 with G = 16: two 8-dim pieces per lane; D = 128 with G = 1 and
+# 64 slots: four rows per wave, each with a full wave of slots)
+FSA_SMALL = SMALL + [(1, 4, 1, 1056, 64, 32, 33), (1, 8, 2, 1280, 128, 64, 20),
+                     (1, 16, 1, 256, 64, 32, 4), (1, 2, 2, 2048, 128, 32, 64)]
 
 
 @pytest.mark.parametrize("shape", FSA_SMALL, ids=lambda s: "B%dHq%dHkv%dT%dD%dbs%dS%d" % s)
