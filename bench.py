@@ -274,7 +274,16 @@ def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, warm=5, per_launch=10, batch=20):
     return {what: dict(st, query_outer_gathered_gb=gb / 1e9, workspace_gb=ws.numel() / 1e9)}
 
 
-def extra_configs(dev, nsa_c5=None):
+def tra_evaluated_weights(B, H, T, rows_per_wave=32, keys_per_tile=64):
+    """Weights the forward kernel evaluates (epilogue elements): each wave of 32 query rows
+    runs every 64-key tile up to the one holding its last row, masked keys included."""
+    r0 = np.arange(0, T, rows_per_wave)
+    last = np.minimum(r0 + rows_per_wave, T) - 1
+    tiles = last // keys_per_tile + 1
+    return float(B * H * rows_per_wave * keys_per_tile * tiles.sum())
+
+
+def extra_configs(dev, nsa_c5=None, ceilings=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
@@ -290,7 +299,16 @@ def extra_configs(dev, nsa_c5=None):
     for pw in (1.0, 2.0, 1.5):
         st = timed(lambda: cat.tra_fwd(q, k, v, 1.0, pw, out=out), batch=200)
         tf = fl / (st["ms"] * 1e-3) / 1e12
-        res[f"tra_fwd B4 H16 T2048 D64 p{pw:g}"] = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
+        r = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
+        if pw == 1.5:
+            # the general power costs one v_log_f32 and one v_exp_f32 per evaluated weight
+            ops = 2.0 * tra_evaluated_weights(B, H, T)
+            r["transcendental_ops"] = ops
+            r["transcendental_ops_per_s"] = ops / (st["ms"] * 1e-3)
+            if ceilings is not None:
+                r["frac_of_measured_log_exp_rate"] = (r["transcendental_ops_per_s"] /
+                                                      ceilings["log_exp_lane_ops_per_s"])
+        res[f"tra_fwd B4 H16 T2048 D64 p{pw:g}"] = r
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(1, 2, 256, 64, dtype=torch.float32, seed=0))
     out = torch.empty_like(q)
     res["tra_fwd_f32 B1 H2 T256 D64 p2"] = timed(
@@ -563,7 +581,7 @@ def main():
         print("bench: other configurations", file=sys.stderr, flush=True)
         c5 = (lambda: cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n),
               gbytes, (gqn, gkn, gvn, gidx, NSA["block_size"], o_n, lse_n))
-        result["other_configs"] = extra_configs(dev, nsa_c5=c5)
+        result["other_configs"] = extra_configs(dev, nsa_c5=c5, ceilings=ceilings)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(q, k, v, idx_np)
