@@ -314,10 +314,24 @@ int oracle_tda_rows(const void *q1, const void *q2, const void *k1, const void *
     const double lam = lambda < 0.0 ? 0.0 : (lambda > 1.0 ? 1.0 : lambda);
     if (!rows) nrows = total;
     set_threads(nthreads);
+    /* every key row as load_row gives it, computed once (the same values that
+     * loading it again for each query would give) */
+    double *nk1 = (double *)malloc(sizeof(double) * (size_t)(total * D));
+    double *nk2 = (double *)malloc(sizeof(double) * (size_t)(total * D));
+    if (total > 0 && (!nk1 || !nk2)) {
+        free(nk1);
+        free(nk2);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < total; ++r) {
+        load_row(k1, dtype, r, D, normalize, nk1 + r * D);
+        load_row(k2, dtype, r, D, normalize, nk2 + r * D);
+    }
     int bad = 0;
 #pragma omp parallel reduction(| : bad)
     {
-        double *buf = (double *)malloc(sizeof(double) * (size_t)(6 * D));
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(4 * D));
         if (!buf) bad = 1;
 #pragma omp for schedule(dynamic, 4)
         for (int64_t n = 0; n < nrows; ++n) {
@@ -327,15 +341,15 @@ int oracle_tda_rows(const void *q1, const void *q2, const void *k1, const void *
             for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
             if (r < 0 || r >= total) { bad = 1; continue; }
             const int64_t bh = r / T, i = r % T;
-            double *qa = buf, *qb = buf + D, *ka = buf + 2 * D, *kb = buf + 3 * D;
-            double *o1 = buf + 4 * D, *o2 = buf + 5 * D;
+            double *qa = buf, *qb = buf + D;
+            double *o1 = buf + 2 * D, *o2 = buf + 3 * D;
             load_row(q1, dtype, bh * T + i, D, normalize, qa);
             load_row(q2, dtype, bh * T + i, D, normalize, qb);
             const double tau = beta * sqrt(2.0 * log((double)(i + 1)) / (double)D);
             for (int64_t d = 0; d < D; ++d) o1[d] = o2[d] = 0.0;
             for (int64_t j = 0; j <= i; ++j) {
-                load_row(k1, dtype, bh * T + j, D, normalize, ka);
-                load_row(k2, dtype, bh * T + j, D, normalize, kb);
+                const double *ka = nk1 + (bh * T + j) * D;
+                const double *kb = nk2 + (bh * T + j) * D;
                 double s1 = 0.0, s2 = 0.0;
                 for (int64_t d = 0; d < D; ++d) {
                     s1 += qa[d] * ka[d];
@@ -354,6 +368,8 @@ int oracle_tda_rows(const void *q1, const void *q2, const void *k1, const void *
         }
         free(buf);
     }
+    free(nk1);
+    free(nk2);
     return bad ? -1 : 0;
 }
 

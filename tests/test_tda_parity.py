@@ -10,7 +10,7 @@ import oracle
 import causal_attention_tiled_amd as cat
 from causal_attention_tiled_amd import inputs
 
-from _parity import BF16_REL, assert_rows_close, sample_rows
+from _parity import BF16_REL, assert_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -48,23 +48,16 @@ def test_tda_lambda_beta(gpu, lam, beta):
                       f"lam={lam} beta={beta}")
 
 
-def test_tda_config_T8192_D128_dense(gpu):
+def test_tda_config_T8192_D128_all_rows(gpu):
     """B=2 H=32 T=8192 D=128, normalised, beta = D^-1/2, lambda = 0.5, p = 2 (the
-    benchmarked launch): full output on the GPU; against the oracle on every row of the
-    last (b, h) slab plus 1,200 rows drawn from all 64 slabs and the tile-edge positions of
-    every slab."""
+    benchmarked launch): every element of the output against the oracle."""
     c = inputs.CONFIGS["tda_bf16_T8192_D128"]
     print("tda config T8192: inputs", flush=True)
     t5 = inputs.tda_inputs(c["B"], c["H"], c["T"], c["D"], seed=0)
     out = _run(t5, c["beta"], c["lam"], 2.0, c["normalize"], gpu)
-    B, H, T, D = t5[0].shape
-    assert torch.isfinite(out.float()).all()
-    rows = sample_rows(B, H, T, 1200, seed=2,
-                       extra_positions=(0, 1, 31, 32, 63, 64, 255, 256, 4095, T - 1))
-    rows = np.unique(np.concatenate([rows, np.arange(T) + (B * H - 1) * T]))
-    print(f"tda config T8192: oracle on {rows.size} rows", flush=True)
-    ref = oracle.tda_ref(*t5, c["beta"], c["lam"], 2.0, normalize=c["normalize"], rows=rows)
-    assert_rows_close(out.reshape(-1, D)[rows], ref, BF16_REL, "tda T8192")
+    print("tda config T8192: oracle on all 524,288 rows", flush=True)
+    ref = oracle.tda_ref(*t5, c["beta"], c["lam"], 2.0, normalize=c["normalize"])
+    assert_rows_close(out, ref, BF16_REL, "tda T8192")
 
 
 @pytest.mark.parametrize("p", [1.0, 2.0, 1.5])

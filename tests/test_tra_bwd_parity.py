@@ -1,7 +1,6 @@
 """GPU parity of the Threshold Rectified Attention backward (tra_bwd) against the
 fp64 oracle on the same seeded inputs, plus GPU-only properties that must hold bit
 for bit (determinism, causal dependency structure)."""
-import numpy as np
 import pytest
 import torch
 
@@ -9,7 +8,7 @@ import oracle
 import causal_attention_tiled_amd as cat
 from causal_attention_tiled_amd import inputs
 
-from _parity import BF16_REL, assert_rows_close, sample_rows
+from _parity import BF16_REL, assert_rows_close
 
 pytestmark = pytest.mark.gpu
 
@@ -69,25 +68,19 @@ def test_tra_bwd_p_below_one_well_conditioned(gpu):
         assert_rows_close(g[:, :, 1:], r[:, :, 1:], BF16_REL, f"{n} p=0.5")
 
 
-def test_tra_bwd_T8192_D128_dense(gpu):
-    """B=2 H=32 T=8192 D=128, beta=1, p=2 (the forward's measured shape): all three
-    gradients on the GPU; against the oracle on every row of four (b, h) slabs (first and
-    last head of each batch) plus 400 rows drawn from all 64 slabs -- 33,184 dq rows and as
-    many dk/dv rows."""
+def test_tra_bwd_T8192_D128_all_rows(gpu):
+    """B=2 H=32 T=8192 D=128, beta=1, p=2 (the forward's measured shape): every element of
+    dq, dk and dv against the oracle."""
     B, H, T, D = 2, 32, 8192, 128
     print("tra_bwd T8192: inputs", flush=True)
     q, k, v = inputs.tra_inputs(B, H, T, D, seed=0)
     do = _dout(B, H, T, D, seed=1)
     dq, dk, dv = _run(q, k, v, do, 1.0, 2.0, gpu)
-    for g in (dq, dk, dv):
-        assert torch.isfinite(g.float()).all()
-    full = np.concatenate([np.arange(T) + bh * T for bh in (0, H - 1, H, 2 * H - 1)])
-    rows = np.unique(np.concatenate([full, sample_rows(B, H, T, 400, seed=3)]))
-    print(f"tra_bwd T8192: oracle on {rows.size} rows", flush=True)
-    rq, rk, rv = oracle.tra_bwd_ref(q, k, v, do, 1.0, 2.0, qrows=rows, krows=rows)
-    assert_rows_close(dq.reshape(-1, D)[rows], rq, BF16_REL, "dq T8192")
-    assert_rows_close(dk.reshape(-1, D)[rows], rk, BF16_REL, "dk T8192")
-    assert_rows_close(dv.reshape(-1, D)[rows], rv, BF16_REL, "dv T8192")
+    print("tra_bwd T8192: oracle on all 524,288 rows of each gradient", flush=True)
+    rq, rk, rv = oracle.tra_bwd_ref(q, k, v, do, 1.0, 2.0)
+    assert_rows_close(dq, rq, BF16_REL, "dq T8192")
+    assert_rows_close(dk, rk, BF16_REL, "dk T8192")
+    assert_rows_close(dv, rv, BF16_REL, "dv T8192")
 
 
 def test_tra_bwd_deterministic(gpu):
