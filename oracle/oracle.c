@@ -543,7 +543,41 @@ int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void 
     if (!qrows) nq = B * Hq * T;
     if (!krows) nk = B * Hkv * T;
     set_threads(nthreads);
+    /* every query row's (M, l, delta), computed once per call by nsa_row_stats (the
+     * same values that computing them again for each query or key row would give);
+     * l = 0 marks a row with an empty set */
+    double *stats = NULL;
+    if (dq || dk || dv) {
+        stats = (double *)malloc(sizeof(double) * (size_t)(3 * B * Hq * T + 1));
+        if (!stats) return -1;
+    }
     int bad = 0;
+    if (stats) {
+#pragma omp parallel reduction(| : bad)
+        {
+            unsigned char *chosen = (unsigned char *)calloc((size_t)(nblk > 0 ? nblk : 1), 1);
+            if (!chosen) bad = 1;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < B * Hq * T; ++r) {
+                if (!chosen) continue;
+                const int64_t bh = r / T, i = r % T, b = bh / Hq, h = bh % Hq, kv = h / G;
+                const int64_t qrow = (bh * T + i) * D, kvslab = (b * Hkv + kv) * T * D;
+                nsa_attended(block_idx + ((b * Hkv + kv) * T + i) * S, S, nblk, bs, i, chosen);
+                double M = 0.0, l = 0.0, delta = 0.0;
+                if (!nsa_row_stats(q, k, v, dout, dtype, chosen, nblk, bs, i, qrow, kvslab, D,
+                                   scale, &M, &l, &delta))
+                    l = 0.0;
+                stats[3 * r] = M;
+                stats[3 * r + 1] = l;
+                stats[3 * r + 2] = delta;
+            }
+            free(chosen);
+        }
+        if (bad) {
+            free(stats);
+            return -1;
+        }
+    }
 #pragma omp parallel reduction(| : bad)
     {
         unsigned char *chosen = (unsigned char *)calloc((size_t)(nblk > 0 ? nblk : 1), 1);
@@ -559,10 +593,8 @@ int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void 
                 const int64_t bh = r / T, i = r % T, b = bh / Hq, h = bh % Hq, kv = h / G;
                 const int64_t qrow = (bh * T + i) * D, kvslab = (b * Hkv + kv) * T * D;
                 nsa_attended(block_idx + ((b * Hkv + kv) * T + i) * S, S, nblk, bs, i, chosen);
-                double M, l, delta;
-                if (!nsa_row_stats(q, k, v, dout, dtype, chosen, nblk, bs, i, qrow, kvslab, D,
-                                   scale, &M, &l, &delta))
-                    continue;
+                const double M = stats[3 * r], l = stats[3 * r + 1], delta = stats[3 * r + 2];
+                if (l == 0.0) continue;
                 for (int64_t blk = 0; blk < nblk; ++blk) {
                     if (!chosen[blk]) continue;
                     for (int64_t j = blk * bs; j < (blk + 1) * bs && j <= i; ++j) {
@@ -595,11 +627,10 @@ int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void 
                     if (!chosen[blk]) continue;
                     for (int64_t g = 0; g < G; ++g) {
                         const int64_t h = kv * G + g;
-                        const int64_t qrow = ((b * Hq + h) * T + i) * D;
-                        double M, l, delta;
-                        if (!nsa_row_stats(q, k, v, dout, dtype, chosen, nblk, bs, i, qrow,
-                                           kvslab, D, scale, &M, &l, &delta))
-                            continue;
+                        const int64_t qr = (b * Hq + h) * T + i, qrow = qr * D;
+                        const double M = stats[3 * qr], l = stats[3 * qr + 1];
+                        const double delta = stats[3 * qr + 2];
+                        if (l == 0.0) continue;
                         double dot = 0.0, dp = 0.0;
                         for (int64_t d = 0; d < D; ++d) {
                             dot += widen(q, dtype, qrow + d) * widen(k, dtype, kvslab + j * D + d);
@@ -617,5 +648,6 @@ int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void 
         }
         free(chosen);
     }
+    free(stats);
     return bad ? -1 : 0;
 }

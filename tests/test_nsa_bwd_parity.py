@@ -1,7 +1,7 @@
 """GPU parity of the NSA selection-branch backward (nsa_sel_bwd) against the fp64
-oracle on the same seeded inputs: small shapes in full, the T=4096 G=8 and T=32768
-G=16 configurations on sampled rows; plus determinism, set semantics and rows or
-blocks that nothing attends."""
+oracle on the same seeded inputs: small shapes and the T=4096 G=8 configuration in full,
+the T=32768 G=16 configuration on sampled rows; plus determinism, set semantics and rows
+or blocks that nothing attends."""
 import numpy as np
 import pytest
 import torch
@@ -138,7 +138,25 @@ def test_nsa_bwd_slot_set_semantics(gpu):
     assert_rows_close(a[2], ref[2], BF16_REL, "dv set")
 
 
-@pytest.mark.parametrize("name", ["nsa_bf16_T4096_G8", "nsa_bf16_T32768_G16"])
+def test_nsa_bwd_T4096_G8_all_rows(gpu):
+    """B=2 Hq=32 Hkv=4 T=4096 D=128 bs=64 S=16: every element of dq, dk and dv against the
+    oracle."""
+    c = inputs.CONFIGS["nsa_bf16_T4096_G8"]
+    B, Hq, Hkv, T, D, bs, S = c["B"], c["Hq"], c["Hkv"], c["T"], c["D"], c["block_size"], c["S"]
+    print("nsa_bwd T4096: inputs", flush=True)
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
+    do = _dout((B, Hq, T, D), seed=1)
+    dq, dk, dv = _run(q, k, v, idx, bs, do, gpu)
+    print("nsa_bwd T4096: oracle on every row", flush=True)
+    rq, rk, rv = oracle.nsa_bwd_ref(q, k, v, idx, bs, do)
+    assert_rows_close(dq, rq, BF16_REL, "dq T4096", floor=FLOOR,
+                      floor_rows=_single_key_rows(idx, bs, Hq // Hkv))
+    assert_rows_close(dk, rk, BF16_REL, "dk T4096")
+    assert_rows_close(dv, rv, BF16_REL, "dv T4096")
+
+
+@pytest.mark.parametrize("name", ["nsa_bf16_T32768_G16"])
 def test_nsa_bwd_config_sampled(gpu, name):
     c = inputs.CONFIGS[name]
     B, Hq, Hkv, T, D, bs, S = c["B"], c["Hq"], c["Hkv"], c["T"], c["D"], c["block_size"], c["S"]
