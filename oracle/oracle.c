@@ -470,6 +470,15 @@ static int64_t nsa_attended(const int32_t *slots, int64_t S, int64_t nblk, int64
     return na;
 }
 
+/* Whether block blk (0 <= blk < nblk) is in the attended set of a query row whose
+ * S slots are given: the membership test of nsa_attended for one block, without
+ * building the whole set (j <= i holds wherever the key-row loop asks). */
+static int nsa_slot_holds(const int32_t *slots, int64_t S, int64_t blk) {
+    for (int64_t s = 0; s < S; ++s)
+        if (slots[s] == blk) return 1;
+    return 0;
+}
+
 /* Softmax statistics of query row (b, h, i) over its attended set:
  * M = max_j s_j and l = sum_j exp(s_j - M), s_j = scale * q_i . k_j; and
  * delta = sum_j P_j (dout_i . v_j) with P_j = exp(s_j - M) / l.  Returns 0 if
@@ -623,8 +632,7 @@ int oracle_nsa_bwd_rows(const void *q, const void *k, const void *v, const void 
                 const int64_t kvslab = bkv * T * D, blk = j / bs;
                 if (blk >= nblk) continue;
                 for (int64_t i = j; i < T; ++i) {
-                    nsa_attended(block_idx + (bkv * T + i) * S, S, nblk, bs, i, chosen);
-                    if (!chosen[blk]) continue;
+                    if (!nsa_slot_holds(block_idx + (bkv * T + i) * S, S, blk)) continue;
                     for (int64_t g = 0; g < G; ++g) {
                         const int64_t h = kv * G + g;
                         const int64_t qr = (b * Hq + h) * T + i, qrow = qr * D;
