@@ -16,7 +16,10 @@
 // query rows of one (b,h) per workgroup, 8 wavefronts of 32 rows, transposed
 // score tiles (one query per lane, so tau is a per-lane scalar), 64-key tiles of
 // K1, K2 and V staged HBM -> LDS by buffer loads, double-buffered, V read
-// transposed from LDS.
+// transposed from LDS.  At D = 64 and for the general power the score accumulators
+// start at -tau, as in that kernel (so lambda = 0 reproduces it bit for bit); at
+// D = 128 with p = 1 or 2 they start at zero and tau is subtracted in the epilogue,
+// which keeps the interior loop free of spills.
 //
 // Normalisation, as torch.nn.functional.normalize does on the page's bf16 tensors:
 // the row's 2-norm rounded to bf16 (at least 1e-12), then each element divided by
@@ -215,6 +218,14 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
         qnorm(qf2);
     }
     const float tau = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
+    // -tau as the score accumulators' starting value where that pays (the vector-heavy
+    // general power, and D = 64); at D = 128 with p = 1 or 2 the sixteen registers it
+    // holds make the interior loop spill, so tau is subtracted in the epilogue instead
+    constexpr bool kFoldTau = D == 64 || PM == kPowGeneral;
+    f32x16 cinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[r] = kFoldTau ? -tau : 0.0f;
+    const float tsub = kFoldTau ? 0.0f : tau;
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s1 = {}, s2 = {};
+            f32x16 s1 = cinit, s2 = cinit;
             bf16x8 pf[2];
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) s1 = mfma_32x32x16(k_frag(K1B, buf, kb, ds), qf1[ds], s1);
@@ -260,8 +271,8 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
 #pragma clang fp contract(off)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float w1 = relu_pow<PM>(s1[r] - tau, p);
-                    const float w2 = relu_pow<PM>(s2[r] - tau, p);
+                    const float w1 = relu_pow<PM>(kFoldTau ? s1[r] : s1[r] - tsub, p);
+                    const float w2 = relu_pow<PM>(kFoldTau ? s2[r] : s2[r] - tsub, p);
                     pf[r >> 3][r & 7] = (__bf16)__builtin_fmaf(-lam, w2, w1);
                 }
             }
