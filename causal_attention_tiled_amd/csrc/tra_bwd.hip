@@ -54,6 +54,21 @@ __device__ __forceinline__ float relu_pow_m1(float x, float p) {
     }
 }
 
+// The weight max(x, 0)^p and max(x, 0)^(p-1) (0 for x <= 0) of one score, as
+// relu_pow and relu_pow_m1 give them; the general power takes log2 max(x, 0) once
+// for both.
+template <int PM>
+__device__ __forceinline__ void relu_pow_both(float x, float p, float &w, float &g) {
+    if constexpr (PM == kPowGeneral) {
+        const float l = __builtin_amdgcn_logf(fmaxf(x, 0.0f));
+        w = __builtin_amdgcn_exp2f(p * l);
+        g = x > 0.0f ? __builtin_amdgcn_exp2f((p - 1.0f) * l) : 0.0f;
+    } else {
+        w = relu_pow<PM>(x, p);
+        g = relu_pow_m1<PM>(x, p);
+    }
+}
+
 // Workgroup id -> (head slab, key tile) for the dk/dv kernel: key tiles with the
 // most queries after them (small index) first; heads split over the 8 XCDs as in
 // tile_order.
@@ -421,8 +436,10 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
             for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(orow[ds], vf[ds], dp);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                wf[r >> 3][r & 7] = (__bf16)relu_pow<PM>(s[r], p);
-                s[r] = relu_pow_m1<PM>(s[r], p);
+                float w, g;
+                relu_pow_both<PM>(s[r], p, w, g);
+                wf[r >> 3][r & 7] = (__bf16)w;
+                s[r] = g;
             }
 #pragma unroll
             for (int i = 0; i < NDS; ++i) {
