@@ -17,8 +17,10 @@
 //    accumulator's register order) and dQ^T += K^T A^T with K^T read transposed
 //    from LDS, each operand read just before its product so that the Q and dO
 //    operands and the dQ accumulator leave room for two waves per SIMD; the
-//    other wave of the SIMD covers the read latency.  K and V tiles stream
-//    HBM -> LDS by DMA, double-buffered, as in the forward.
+//    other wave of the SIMD covers the read latency.  At D = 64 the S and dP
+//    chains are interleaved instead, with each step's K and V rows read one step
+//    ahead.  K and V tiles stream HBM -> LDS by DMA, double-buffered, as in the
+//    forward.
 //  * tra_bwd_dkv_kernel: 128 key rows per workgroup, 4 wavefronts of 32 keys, one
 //    per SIMD (the dK and dV accumulators take 128 registers per lane).  A wave
 //    keeps its K and V rows in registers; Q and dO tiles of 64 queries stream
@@ -212,11 +214,34 @@ __global__ __launch_bounds__(64 * kDqWaves) void tra_bwd_dq_kernel(
         for (int kb = 0; kb < 2; ++kb) {
             f32x16 s = {}, dp = {};
             bf16x8 af[2];
+            if constexpr (D == 64) {
+                // the S and dP chains interleaved, each step's K and V rows read one step
+                // ahead of its products (fenced so the compiler keeps the order); at
+                // D = 64 this also leaves room for three waves per SIMD
+                bf16x8 kr = row_frag(KB, buf, kb, 0), vr = row_frag(VB, buf, kb, 0);
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(row_frag(KB, buf, kb, ds), qf[ds], s);
-            if constexpr (kMasked) mask_block(s, n * kBN + 32 * kb);
+                for (int ds = 0; ds < NDS; ++ds) {
+                    bf16x8 kn = kr, vn = vr;
+                    if (ds + 1 < NDS) {
+                        kn = row_frag(KB, buf, kb, ds + 1);
+                        vn = row_frag(VB, buf, kb, ds + 1);
+                    }
+                    s = mfma_32x32x16(kr, qf[ds], s);
+                    dp = mfma_32x32x16(vr, df[ds], dp);
+                    __builtin_amdgcn_sched_barrier(0);
+                    kr = kn;
+                    vr = vn;
+                }
+                if constexpr (kMasked) mask_block(s, n * kBN + 32 * kb);
+            } else {
+                // at D = 128 each operand is read just before its product: the registers
+                // a read-ahead needs make the kernel spill
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(row_frag(VB, buf, kb, ds), df[ds], dp);
+                for (int ds = 0; ds < NDS; ++ds) s = mfma_32x32x16(row_frag(KB, buf, kb, ds), qf[ds], s);
+                if constexpr (kMasked) mask_block(s, n * kBN + 32 * kb);
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) dp = mfma_32x32x16(row_frag(VB, buf, kb, ds), df[ds], dp);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = relu_pow_m1<PM>(s[r] - tau, p);
 #pragma unroll
