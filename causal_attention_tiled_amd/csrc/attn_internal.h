@@ -48,7 +48,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (bf16: 32 rows per wavefront; 8 wavefronts at D = 128, 4 at D = 64).
 constexpr int tra_bf16_waves(int D) { return D == 128 ? 8 : 4; }
 constexpr int tra_bf16_rows(int D) { return 32 * tra_bf16_waves(D); }
-constexpr int kTraF32Rows = 16;
+constexpr int kTraF32Rows = 8;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;
 // Key rows per workgroup of the Threshold Rectified Attention backward's dk/dv kernel.

@@ -40,7 +40,7 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;    // fp32 kernel
+constexpr int kThreads = 512;    // fp32 kernel: 16 key slices of 32 lanes
 constexpr int kQueryBlocks = 1;  // bf16 kernel: 32-row query blocks per wave
 constexpr int kBN = 64;   // keys per LDS tile
 
@@ -360,21 +360,23 @@ __global__ __launch_bounds__(64 * NW) void tra_fwd_bf16_kernel(
     }
 }
 
-// fp32 kernel: 16 query rows per workgroup; each wave takes one quarter of every key
-// tile for all 16 rows (4 lanes per row, each a quarter of the head dim), and the four
-// partial outputs are summed through LDS at the end.  K/V tiles of 64 keys are staged
+// fp32 kernel: 8 query rows per workgroup of 512 threads; each group of 32 lanes (a
+// key slice, two per wave) takes one sixteenth of every 64-key tile for all 8 rows
+// (4 lanes per row, each a quarter of the head dim), and the sixteen partial outputs
+// are summed through LDS at the end, in slice order.  K/V tiles of 64 keys are staged
 // in LDS; all arithmetic is fp32.
 template <int D, int PM>
 __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, int T, int nqt, float beta, float p) {
     constexpr int BQ = kTraF32Rows, BK = 64, DPT = D / 4;
-    constexpr int NSL = kThreads / (BQ * 4);     // key slices (waves) per workgroup
+    constexpr int NSL = kThreads / (BQ * 4);     // key slices per workgroup
     constexpr int KS = BK / NSL;                 // keys of a tile per slice
     static_assert(NSL * BQ * 4 == kThreads && KS % 4 == 0, "slices");
-    static_assert(NSL * BQ * D <= BK * D, "the reduction reuses the K tile");
-    __shared__ __attribute__((aligned(16))) float Ksh[BK][D];
-    __shared__ __attribute__((aligned(16))) float Vsh[BK][D];
+    static_assert(NSL * BQ * D <= 2 * BK * D, "the reduction reuses the K and V tiles");
+    __shared__ __attribute__((aligned(16))) float KVsh[2][BK][D];
+    float (&Ksh)[BK][D] = KVsh[0];
+    float (&Vsh)[BK][D] = KVsh[1];
 
     const int bh = blockIdx.x / nqt;
     const int qt = nqt - 1 - blockIdx.x % nqt;
@@ -396,17 +398,19 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
 
     // K/V tile staging: 16-byte pieces, all of a thread's loads issued before its LDS
     // stores, and the next tile's loads issued before the current tile is computed
-    constexpr int PER = BK * D / 4 / kThreads;  // float4 pieces per thread per tensor
+    constexpr int PER = BK * D / 4 / kThreads;  // 4-float pieces per thread per tensor
     static_assert(BK * D % (4 * kThreads) == 0, "tile staging");
-    float4 kr[PER], vr[PER];
+    // native 4-float vectors: with HIP's float4 struct the prefetched pieces went
+    // through private memory
+    f32x4 kr[PER], vr[PER];
     auto fetch = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = (tid + i * kThreads) * 4;
             const int key = k0 + e / D;
-            const float4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-            kr[i] = key < T ? *(const float4 *)(K + slab + (size_t)key * D + e % D) : z;
-            vr[i] = key < T ? *(const float4 *)(V + slab + (size_t)key * D + e % D) : z;
+            const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+            kr[i] = key < T ? *(const f32x4 *)(K + slab + (size_t)key * D + e % D) : z;
+            vr[i] = key < T ? *(const f32x4 *)(V + slab + (size_t)key * D + e % D) : z;
         }
     };
     fetch(0);
@@ -415,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = (tid + i * kThreads) * 4;
-            *(float4 *)(&Ksh[e / D][e % D]) = kr[i];
-            *(float4 *)(&Vsh[e / D][e % D]) = vr[i];
+            *(f32x4 *)(&Ksh[e / D][e % D]) = kr[i];
+            *(f32x4 *)(&Vsh[e / D][e % D]) = vr[i];
         }
         __syncthreads();
         if (k0 + BK <= q_last) fetch(k0 + BK);
@@ -446,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void tra_fwd_f32_kernel(
     }
     // sum the slices' partial outputs (in slice order) through the K tile's LDS
     __syncthreads();
-    float *red = &Ksh[0][0];  // [slice][row][D]
+    float *red = &KVsh[0][0][0];  // [slice][row][D]
 #pragma unroll
     for (int d = 0; d < DPT; ++d) red[(slice * BQ + row) * D + part * DPT + d] = acc[d];
     __syncthreads();
