@@ -16,10 +16,10 @@
 // query rows of one (b,h) per workgroup, 8 wavefronts of 32 rows, transposed
 // score tiles (one query per lane, so tau is a per-lane scalar), 64-key tiles of
 // K1, K2 and V staged HBM -> LDS by buffer loads, double-buffered, V read
-// transposed from LDS.  At D = 64 and for the general power the score accumulators
-// start at -tau, as in that kernel (so lambda = 0 reproduces it bit for bit); at
-// D = 128 with p = 1 or 2 they start at zero and tau is subtracted in the epilogue,
-// which keeps the interior loop free of spills.
+// transposed from LDS.  The score accumulators start at -tau, as in that kernel (so
+// lambda = 0 reproduces it bit for bit).  At D = 128 the Q2^T operands are read from
+// a copy of the workgroup's Q2 rows in LDS instead of being held in registers, which
+// leaves room for the -tau registers without spilling.
 //
 // Normalisation, as torch.nn.functional.normalize does on the page's bf16 tensors:
 // the row's 2-norm rounded to bf16 (at least 1e-12), then each element divided by
@@ -111,7 +111,11 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
     static_assert(TILEB == kWaves * LOADS * 1024, "one 1 KB DMA block per wave and chunk");
     static_assert(K2B + TILEB + BLKB + 32 * ROWB <= 65536, "K immediate offsets");
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[6 * TILEB];
+    // At D = 128 the Q2^T operands live in LDS (the workgroup's Q2 rows, after the K/V
+    // tiles: 160 KB in all), which frees the registers that let the scores start at -tau
+    constexpr bool kQ2Lds = D == 128;
+    constexpr int Q2B = 6 * TILEB;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[6 * TILEB + (kQ2Lds ? BM * ROWB : 0)];
 
     int bh, qt;
     tile_order(blockIdx.x, BH, nqt, bh, qt);
@@ -217,15 +221,27 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
         qnorm(qf1);
         qnorm(qf2);
     }
+    // Q2^T operands: this wave's 32 rows at rows 32*wave + l32 of the LDS copy, in the
+    // K tiles' chunk order
+    int q2off[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) q2off[ds] = Q2B + wave * 32 * ROWB + koff[ds];
+    if constexpr (kQ2Lds) {
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) *(bf16x8 *)(&lds[q2off[ds]]) = qf2[ds];
+    }
+    auto q2_frag = [&](int ds) {
+        if constexpr (kQ2Lds)
+            return *(const bf16x8 *)(&lds[q2off[ds]]);
+        else
+            return qf2[ds];
+    };
     const float tau = beta * sqrtf(2.0f * logf((float)(myq + 1)) / (float)D);
-    // -tau as the score accumulators' starting value where that pays (the vector-heavy
-    // general power, and D = 64); at D = 128 with p = 1 or 2 the sixteen registers it
-    // holds make the interior loop spill, so tau is subtracted in the epilogue instead
-    constexpr bool kFoldTau = D == 64 || PM == kPowGeneral;
+    // -tau as the score accumulators' starting value (sixteen registers feeding the
+    // first MFMA of each chain as its C operand): no subtraction per score
     f32x16 cinit;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = kFoldTau ? -tau : 0.0f;
-    const float tsub = kFoldTau ? 0.0f : tau;
+    for (int r = 0; r < 16; ++r) cinit[r] = -tau;
 
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) expcnt(7) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) s1 = mfma_32x32x16(k_frag(K1B, buf, kb, ds), qf1[ds], s1);
 #pragma unroll
-            for (int ds = 0; ds < NDS; ++ds) s2 = mfma_32x32x16(k_frag(K2B, buf, kb, ds), qf2[ds], s2);
+            for (int ds = 0; ds < NDS; ++ds) s2 = mfma_32x32x16(k_frag(K2B, buf, kb, ds), q2_frag(ds), s2);
             if constexpr (kMasked) {
                 mask_block(s1, n * kBN + 32 * kb);
                 mask_block(s2, n * kBN + 32 * kb);
@@ -271,8 +287,8 @@ __global__ __launch_bounds__(64 * kWaves) void tda_fwd_bf16_kernel(
 #pragma clang fp contract(off)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float w1 = relu_pow<PM>(kFoldTau ? s1[r] : s1[r] - tsub, p);
-                    const float w2 = relu_pow<PM>(kFoldTau ? s2[r] : s2[r] - tsub, p);
+                    const float w1 = relu_pow<PM>(s1[r], p);
+                    const float w2 = relu_pow<PM>(s2[r], p);
                     pf[r >> 3][r & 7] = (__bf16)__builtin_fmaf(-lam, w2, w1);
                 }
             }
