@@ -74,7 +74,7 @@ __device__ __forceinline__ void relu_pow_both(float x, float p, float &w, float 
 // Workgroup id -> (head slab, key tile) for the dk/dv kernel: key tiles with the
 // most queries after them (small index) first; heads split over the 8 XCDs as in
 // tile_order.
-__device__ __forceinline__ void key_tile_order(int bid, int BH, int nkt, int &bh, int &kt) {
+__device__ __forceinline__ void key_tile_order(int bid, int BH, int &bh, int &kt) {
     if ((BH & 7) == 0) {
         const int xcd = bid & 7, s = bid >> 3, hpx = BH >> 3;
         bh = xcd * hpx + s % hpx;
@@ -289,7 +289,7 @@ template <int D, int PM>
 __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO, uint16_t *__restrict__ dK,
-    uint16_t *__restrict__ dV, int BH, int T, int nkt, float beta, float p) {
+    uint16_t *__restrict__ dV, int BH, int T, float beta, float p) {
     constexpr int BK = kDkvWaves * 32;               // key rows per workgroup
     constexpr int ROWB = D * 2;
     constexpr int CH = D / 8;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
     __shared__ __attribute__((aligned(16))) float ntau[2][kBN];  // -tau of each query of a tile
 
     int bh, kt;
-    key_tile_order(blockIdx.x, BH, nkt, bh, kt);
+    key_tile_order(blockIdx.x, BH, bh, kt);
     bh = __builtin_amdgcn_readfirstlane(bh);
     kt = __builtin_amdgcn_readfirstlane(kt);
     const int tid = threadIdx.x;
@@ -552,7 +552,7 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
                                    dim3((unsigned)(BH * nqt)), dim3(64 * W), a1, 0, stream);
     if (e != hipSuccess) return e;
     int nkt = (T + kTraBwdDkvRows - 1) / kTraBwdDkvRows;
-    void *a2[] = {&q, &k, &v, &dout, &dk, &dv, &BH, &T, &nkt, &beta, &p};
+    void *a2[] = {&q, &k, &v, &dout, &dk, &dv, &BH, &T, &beta, &p};
     return hipLaunchKernel((const void *)tra_bwd_dkv_kernel<D, PM>, dim3((unsigned)(BH * nkt)),
                            dim3(64 * kDkvWaves), a2, 0, stream);
 }
