@@ -73,6 +73,14 @@ def test_tra_config_f32_T256(gpu):
     assert_rows_close(out, oracle.tra_ref(q, k, v, c["beta"], 2.0), F32_REL, "f32 T256")
 
 
+@pytest.mark.parametrize("p", [2.0, 1.5])
+def test_tra_f32_T1024_D128(gpu, p):
+    """fp32, B=1 H=2 T=1024 D=128, beta=1: 16 key tiles per row block, every element."""
+    q, k, v = inputs.tra_inputs(1, 2, 1024, 128, dtype=torch.float32, seed=3)
+    out = _run_f32(q, k, v, 1.0, p, gpu)
+    assert_rows_close(out, oracle.tra_ref(q, k, v, 1.0, p), F32_REL, f"f32 T1024 D128 p={p}")
+
+
 @pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
 def test_tra_config_bf16_T2048_D64(gpu, p):
     """bf16, B=4 H=16 T=2048 D=64, beta=1, p in {1, 2, 1.5}: every element."""
