@@ -24,8 +24,12 @@ def _run(q, k, v, do, beta, p, dev):
     return [x.cpu() for x in g]
 
 
+# At D = 128 the dk/dv kernel takes 256 keys per workgroup (64 per wave): T = 256, 257, 511
+# and 1000 give an exact workgroup, one holding a single key, waves whose keys all lie
+# past T, and a ragged last workgroup.
 SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 1, 129, 64), (1, 2, 300, 128),
-         (2, 1, 520, 64), (1, 1, 777, 128)]
+         (2, 1, 520, 64), (1, 1, 777, 128), (1, 1, 256, 128), (1, 2, 257, 128), (2, 1, 511, 128),
+         (1, 1, 1000, 128)]
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
