@@ -87,6 +87,21 @@ def test_tra_bwd_T8192_D128_all_rows(gpu):
     assert_rows_close(dv, rv, BF16_REL, "dv T8192")
 
 
+@pytest.mark.parametrize("p", [2.0, 1.5])
+def test_tra_bwd_T2048_D64_all_rows(gpu, p):
+    """B=4 H=16 T=2048 D=64, beta=1 (the D = 64 forward's shape): every element of dq, dk
+    and dv against the oracle."""
+    B, H, T, D = 4, 16, 2048, 64
+    print(f"tra_bwd T2048 D64 p={p}", flush=True)
+    q, k, v = inputs.tra_inputs(B, H, T, D, seed=2)
+    do = _dout(B, H, T, D, seed=3)
+    dq, dk, dv = _run(q, k, v, do, 1.0, p, gpu)
+    rq, rk, rv = oracle.tra_bwd_ref(q, k, v, do, 1.0, p)
+    assert_rows_close(dq, rq, BF16_REL, f"dq T2048 D64 p={p}")
+    assert_rows_close(dk, rk, BF16_REL, f"dk T2048 D64 p={p}")
+    assert_rows_close(dv, rv, BF16_REL, f"dv T2048 D64 p={p}")
+
+
 def test_tra_bwd_deterministic(gpu):
     q, k, v = inputs.tra_inputs(2, 2, 700, 128, seed=5)
     do = _dout(2, 2, 700, 128, seed=6)
