@@ -103,7 +103,7 @@ ATTN_EXPORT int tra_bwd(const void *q, const void *k, const void *v, const void 
                         void *dk, void *dv, int B, int H, int T, int D, float beta, float p,
                         void *stream) {
     bool noop;
-    const int st = tra_validate(q, k, v, dq, B, H, T, D, beta, p, attn::kTraBwdDkvRows, &noop);
+    const int st = tra_validate(q, k, v, dq, B, H, T, D, beta, p, attn::tra_bwd_dkv_rows(D), &noop);
     if (st != ATTN_OK || noop) return st;
     if (!bf16_slab_fits(T, D)) return ATTN_ERR_UNSUPPORTED;
     if (!dout || !dk || !dv) return ATTN_ERR_NULL;

@@ -51,8 +51,10 @@ constexpr int tra_bf16_rows(int D) { return 32 * tra_bf16_waves(D); }
 constexpr int kTraF32Rows = 8;
 // Query rows per workgroup of the Threshold Differential Attention kernel.
 constexpr int kTdaRows = 256;
-// Key rows per workgroup of the Threshold Rectified Attention backward's dk/dv kernel.
-constexpr int kTraBwdDkvRows = 128;
+// Key rows per workgroup of the Threshold Rectified Attention backward's dk/dv kernels
+// (64 keys per wave at D = 128, 32 at D = 64; four waves).  The dq kernel's workgroups
+// take as many query rows, so this also sizes the larger of the two grids.
+constexpr int tra_bwd_dkv_rows(int D) { return D == 128 ? 256 : 128; }
 
 // Host-side launchers (one per kernel family); they pick the template
 // instance and return the HIP launch status.

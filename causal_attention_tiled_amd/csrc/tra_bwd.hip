@@ -46,7 +46,7 @@ namespace {
 template <int D>
 constexpr int dq_waves() { return D == 128 ? 8 : 4; }
 constexpr int kDkvWaves = 4;  // dk/dv kernel: 32 key rows per wave
-static_assert(kDkvWaves * 32 == kTraBwdDkvRows, "dk/dv workgroup rows");
+static_assert(kDkvWaves * 32 == tra_bwd_dkv_rows(64), "dk/dv workgroup rows");
 constexpr int kBN = 64;       // keys (dq kernel) or queries (dk/dv kernel) per LDS tile
 
 // max(x, 0)^(p-1) for x > 0, else 0 (the factor p is applied to the sums).
@@ -557,6 +557,7 @@ __device__ __forceinline__ void mfma_acc(f32x16 &acc, bf16x8 a, bf16x8 b) {
 }
 
 constexpr int kDkvWideWaves = 4;  // 64 keys per wave, one wave per SIMD
+static_assert(kDkvWideWaves * 64 == tra_bwd_dkv_rows(128), "dk/dv workgroup rows");
 
 // dK/dV for D = 128 with 64 keys per wave.  The accumulators of 64 keys x 128 dims
 // (dK and dV: 256 fp32 registers per lane) fill the accumulation registers, so
@@ -862,11 +863,11 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
     if (e != hipSuccess) return e;
     void *a2[] = {&q, &k, &v, &dout, &dk, &dv, &BH, &T, &beta, &p};
     if constexpr (D == 128) {
-        int nkt = (T + 64 * kDkvWideWaves - 1) / (64 * kDkvWideWaves);
+        int nkt = (T + tra_bwd_dkv_rows(D) - 1) / tra_bwd_dkv_rows(D);
         return hipLaunchKernel((const void *)tra_bwd_dkv_wide_kernel<D, PM>,
                                dim3((unsigned)(BH * nkt)), dim3(64 * kDkvWideWaves), a2, 0, stream);
     } else {
-        int nkt = (T + kTraBwdDkvRows - 1) / kTraBwdDkvRows;
+        int nkt = (T + tra_bwd_dkv_rows(D) - 1) / tra_bwd_dkv_rows(D);
         return hipLaunchKernel((const void *)tra_bwd_dkv_kernel<D, PM>, dim3((unsigned)(BH * nkt)),
                                dim3(64 * kDkvWaves), a2, 0, stream);
     }
