@@ -551,7 +551,10 @@ __global__ __launch_bounds__(64 * kDkvWaves) void tra_bwd_dkv_kernel(
 // products keep the vector-register form.  The compiler does not see an MFMA here,
 // so the hazards it would otherwise cover are handled in place: the B operand (W or
 // A, just written by VALU instructions) needs two wait states before the MFMA
-// reads it (s_nop 1); back-to-back accumulation into the same tuple needs none.
+// reads it (s_nop 1); back-to-back accumulation into the same tuple needs none.  These
+// are the distances the compiler keeps between its own MFMAs and their producers on
+// this target (two wait states after v_cvt_pk_bf16_f32; dependent accumulations issued
+// back to back).
 __device__ __forceinline__ void mfma_acc(f32x16 &acc, bf16x8 a, bf16x8 b) {
     asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
