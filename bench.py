@@ -14,9 +14,12 @@ Per-launch kernel durations come from HIP events recorded on the stream the
 kernels run on.  After the timed steps, the other configurations of the method
 (TRA at T=2048 D=64 for p = 1, 2, 1.5; TRA fp32 at T=256; Threshold Differential
 Attention at T=8192 D=128; the TRA backward at T=8192 D=128; NSA G=8 at T=4096;
-NSA G=16 at T=32768 with caches flushed before each launch) are timed on their
-own
-and reported under "other_configs".  Prints ONE JSON line.
+NSA G=16 at T=32768 with caches flushed before each launch, the NSA backward and
+block-outer forward at both NSA shapes) are timed on their own and reported under
+"other_configs"; the rows beyond the two forwards (TDA, the TRA backward, the NSA
+backward and block-outer forward) carry a "roofline" entry and, unless
+--no-cpu-baseline, the oracle timed on a bounded sample as "cpu_baseline".  Prints ONE
+JSON line.
 """
 from __future__ import annotations
 
@@ -81,17 +84,65 @@ def nsa_gathered_bytes(idx, T, bs, D, rows_kv=None):
     return float(distinct.sum()) * 2 * bs * D * 2
 
 
-def nsa_useful_flops(idx, T, bs, D, G):
-    """4*D FLOPs (q.k and p*v) per (query head, attended token): the attended tokens of
-    query i are those j <= i of its distinct, in-range selected blocks."""
+def nsa_tokens(idx, T, bs, rows_kv=None):
+    """Attended tokens of each (b, kv head, query) row (flat (b*Hkv+kv)*T+i ids, else all
+    rows): the j <= i of the row's distinct, in-range selected blocks."""
     nblk = T // bs
     flat = idx.reshape(-1, idx.shape[-1])
-    pos = (np.arange(flat.shape[0]) % T)[:, None]
+    if rows_kv is not None:
+        flat = flat[np.asarray(rows_kv)]
+        pos = (np.asarray(rows_kv) % T)[:, None]
+    else:
+        pos = (np.arange(flat.shape[0]) % T)[:, None]
     srt = np.sort(flat, axis=1)
     first = np.concatenate([np.ones((srt.shape[0], 1), bool), srt[:, 1:] != srt[:, :-1]], axis=1)
     ok = first & (srt >= 0) & (srt < nblk) & (srt * bs <= pos)
-    tokens = np.where(ok, np.minimum(bs, pos - srt * bs + 1), 0).sum()
-    return 4.0 * D * G * float(tokens)
+    return np.where(ok, np.minimum(bs, pos - srt * bs + 1), 0).sum(axis=1)
+
+
+def nsa_useful_flops(idx, T, bs, D, G):
+    """4*D FLOPs (q.k and p*v) per (query head, attended token)."""
+    return 4.0 * D * G * float(nsa_tokens(idx, T, bs).sum())
+
+
+def nsa_key_pairs(idx, T, bs, G, krows):
+    """(query head, query) pairs that attend each key row (flat (b*Hkv+kv)*T+j ids): G for
+    every query i >= j whose selection holds the key's block."""
+    Hkv = idx.shape[1]
+    out = np.empty(len(krows))
+    for n, r in enumerate(np.asarray(krows)):
+        bk, j = divmod(int(r), T)
+        b, kv = divmod(bk, Hkv)
+        out[n] = G * np.count_nonzero((idx[b, kv, j:, :] == j // bs).any(axis=1))
+    return out
+
+
+def mfma_roofline(flops, ms, note):
+    """Roofline entry of a kernel bound by the bf16 matrix units: useful FLOPs per launch
+    over the launch time against the published dense peak."""
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / PEAK_BF16_TFLOPS, "per_launch": note}
+
+
+def oracle_rate(fn, budget_s, n0, nmax):
+    """The fp64 oracle on growing samples: fn(n) draws n rows, runs the oracle on them and
+    returns (seconds in the oracle call, work of those rows); n doubles until budget_s of
+    oracle time is spent.  Returns (work per second, rows, seconds)."""
+    n, spent, work, nrows = n0, 0.0, 0.0, 0
+    while spent < budget_s and n <= nmax:
+        s, w = fn(n)
+        spent += s
+        work += w
+        nrows += n
+        n *= 2
+    return work / spent, nrows, spent
+
+
+def oracle_entry(value, unit, sample):
+    import oracle
+    return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": sample}
 
 
 def nsa_unique_bytes(B, Hq, Hkv, T, D, S):
@@ -241,9 +292,18 @@ def timed(fn, warm=10, per_launch=20, batch=50):
     return st
 
 
-def nsa_bwd(dev, q, k, v, gidx, bs, o, lse, gb, G, what, warm=5, per_launch=10, batch=10):
+def nsa_bwd_unique_bytes(B, Hq, Hkv, T, D, S):
+    """Bytes every nsa_sel_bwd launch must move at least once: q, out, dout, lse, k, v and
+    block_idx read, dq, dk, dv written."""
+    return float(4 * B * Hq * T * D * 2 + 4 * B * Hkv * T * D * 2 + B * Hq * T * 4 + B * Hkv * T * S * 4)
+
+
+def nsa_bwd(dev, q, k, v, gidx, bs, o, lse, gb, G, what, fwd_flops, warm=5, per_launch=10,
+            batch=10):
     """Time nsa_sel_bwd on the forward's inputs; algorithmic bytes = the forward's gathered
-    K/V bytes plus 2*G*D*2 bytes of q and dout per (group, query, block) visit."""
+    K/V bytes plus 2*G*D*2 bytes of q and dout per (group, query, block) visit.  Useful
+    FLOPs: 10*D per (query head, attended token) (S, dP, dV, dK, dQ), i.e. 2.5x the
+    forward's."""
     do = torch.randn(*q.shape, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev)
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
@@ -254,11 +314,15 @@ def nsa_bwd(dev, q, k, v, gidx, bs, o, lse, gb, G, what, warm=5, per_launch=10, 
     st = timed(lambda: cat.nsa_sel_bwd(q, k, v, gidx, bs, o, lse, do, dq=g[0], dk=g[1], dv=g[2],
                                        workspace=ws), warm, per_launch, batch)
     total = gb * (1.0 + G / bs)
+    fl = 2.5 * fwd_flops
+    ub = nsa_bwd_unique_bytes(B, Hq, Hkv, T, D, S)
+    roof = mfma_roofline(fl, st["ms"], f"{fl:.5g} useful FLOPs ({fl / PEAK_BF16_TFLOPS / 1e9:.4f} ms "
+                         f"at peak) and {ub:.5g} unique bytes ({ub / PEAK_HBM_GBPS / 1e6:.4f} ms at peak)")
     return {what: dict(st, algorithmic_gb=total / 1e9, gbps=total / (st["ms"] * 1e-3) / 1e9,
-                       workspace_gb=ws.numel() / 1e9)}
+                       workspace_gb=ws.numel() / 1e9, roofline=roof)}
 
 
-def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, warm=5, per_launch=10, batch=20):
+def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, flops, warm=5, per_launch=10, batch=20):
     """Time the block-outer forward (same outputs as nsa_sel_fwd) on the same inputs.  It
     reads each selected block once per list segment rather than once per query, so the
     query-outer kernel's gathered bytes are given for reference, not as its traffic."""
@@ -271,7 +335,54 @@ def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, warm=5, per_launch=10, batch=20):
                      device=dev)
     st = timed(lambda: cat.nsa_sel_fwd_fsa(q, k, v, gidx, bs, out=o, lse=lse, workspace=ws),
                warm, per_launch, batch)
-    return {what: dict(st, query_outer_gathered_gb=gb / 1e9, workspace_gb=ws.numel() / 1e9)}
+    ub = nsa_unique_bytes(B, Hq, Hkv, T, D, S)
+    roof = mfma_roofline(flops, st["ms"], f"{flops:.5g} useful FLOPs ({flops / PEAK_BF16_TFLOPS / 1e9:.4f} "
+                         f"ms at peak) and {ub:.5g} unique bytes ({ub / PEAK_HBM_GBPS / 1e6:.4f} ms at peak)")
+    return {what: dict(st, query_outer_gathered_gb=gb / 1e9, workspace_gb=ws.numel() / 1e9,
+                       roofline=roof)}
+
+
+def nsa_oracle_rates(cpu, fsa_entry, bwd_entry, rng, budget_s=3.0):
+    """The oracle on bounded samples of the headline NSA workload (B1 Hq64 Hkv4 T32768 G16),
+    in useful TFLOP/s: the forward (which the block-outer form computes too) at 4*D per
+    (query head, attended token), and the backward at 10*D per pair, counted 5*D on the
+    dq side for each sampled query row's pairs and 5*D on the dk/dv side for each sampled
+    key row's pairs (key rows drawn at the same fraction of all key rows)."""
+    import oracle
+    q, k, v, idx = cpu["q"], cpu["k"], cpu["v"], cpu["idx"]
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    G, bs = Hq // Hkv, NSA["block_size"]
+
+    def kv_rows(rows):
+        bh = rows // T
+        return ((bh // Hq) * Hkv + (bh % Hq) // G) * T + rows % T
+
+    def fwd(n):
+        rows = rng.integers(0, B * Hq * T, size=n)
+        t0 = time.perf_counter()
+        oracle.nsa_ref(q, k, v, idx, bs, rows=rows)
+        return time.perf_counter() - t0, 4.0 * D * float(nsa_tokens(idx, T, bs, kv_rows(rows)).sum())
+    rate, nrows, spent = oracle_rate(fwd, budget_s, 256, 1 << 18)
+    fsa_entry["cpu_baseline"] = oracle_entry(
+        rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn (head, query) rows of the same "
+        f"workload through the forward oracle ({spent:.1f} s), fp64")
+    dout = torch.randn(*q.shape, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+
+    def bwd(n):
+        qr = rng.integers(0, B * Hq * T, size=n)
+        kr = rng.integers(0, B * Hkv * T, size=max(1, n * Hkv // Hq))
+        t0 = time.perf_counter()
+        oracle.nsa_bwd_ref(q, k, v, idx, bs, dout, qrows=qr, krows=kr)
+        s = time.perf_counter() - t0
+        pairs = float(nsa_tokens(idx, T, bs, kv_rows(qr)).sum() + nsa_key_pairs(idx, T, bs, G, kr).sum())
+        return s, 5.0 * D * pairs
+    # the oracle's key rows recompute the softmax statistics of every attending query row,
+    # so they cost far more than their pairs: small first samples
+    rate, nrows, spent = oracle_rate(bwd, budget_s, 32, 1 << 16)
+    bwd_entry["cpu_baseline"] = oracle_entry(
+        rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn (head, query) rows (dq) and "
+        f"{Hkv}/{Hq} as many (kv head, key) rows (dk, dv) of the same workload ({spent:.1f} s), fp64")
 
 
 def tra_evaluated_weights(B, H, T, rows_per_wave=32, keys_per_tile=64):
@@ -283,14 +394,19 @@ def tra_evaluated_weights(B, H, T, rows_per_wave=32, keys_per_tile=64):
     return float(B * H * rows_per_wave * keys_per_tile * tiles.sum())
 
 
-def extra_configs(dev, nsa_c5=None, ceilings=None):
+def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
     """The other workloads of the method at their own sizes (not the headline line):
     TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
     at T=4096 (forward, block-outer forward and backward); both NSA forwards at B3
     Hq16 T8192 for G = 1, 2, 4, 8, 16; and NSA G=16 at T=32768:
     block-outer forward, backward, and forward with L2 and MALL flushed before every
-    launch."""
+    launch.  TDA, the TRA backward, the NSA backward and the block-outer NSA forward
+    carry a roofline entry; with cpu (the headline NSA inputs on the host, or {} to skip
+    the NSA rows) each also carries the oracle timed on a bounded sample of its rows, in
+    the same unit."""
+    import oracle
+    rng = np.random.default_rng(77)
     res = {}
     B, H, T, D = 4, 16, 2048, 64
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
@@ -315,7 +431,8 @@ def extra_configs(dev, nsa_c5=None, ceilings=None):
         lambda: cat.tra_fwd_f32(q, k, v, 1.0, 2.0, out=out), batch=200)
     c = inputs.CONFIGS["tda_bf16_T8192_D128"]
     B, H, T, D = c["B"], c["H"], c["T"], c["D"]
-    t5 = [x.to(dev) for x in inputs.tda_inputs(B, H, T, D, seed=0)]
+    t5c = inputs.tda_inputs(B, H, T, D, seed=0)
+    t5 = [x.to(dev) for x in t5c]
     ws = torch.empty(cat.tda_workspace_bytes(B, H, T, D, c["normalize"]), dtype=torch.uint8,
                      device=dev)
     out = torch.empty_like(t5[0])
@@ -323,20 +440,47 @@ def extra_configs(dev, nsa_c5=None, ceilings=None):
     st = timed(lambda: cat.tda_fwd(*t5, c["beta"], c["lam"], 2.0, normalize=c["normalize"],
                                    out=out, workspace=ws), batch=20)
     tf = fl / (st["ms"] * 1e-3) / 1e12
-    res["tda_fwd B2 H32 T8192 D128 normalised beta=D^-1/2 lambda=0.5 p2 (6D FLOP per pair)"] = dict(
-        st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
-    del t5, ws, out
+    e = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS,
+             roofline=mfma_roofline(fl, st["ms"], f"{fl:.5g} FLOPs (6*D per causal pair)"))
+    if cpu is not None:
+        def run(n):
+            rows = rng.integers(0, B * H * T, size=n)
+            t0 = time.perf_counter()
+            oracle.tda_ref(*t5c, c["beta"], c["lam"], 2.0, normalize=c["normalize"], rows=rows)
+            return time.perf_counter() - t0, 6.0 * D * float(np.sum(rows % T + 1))
+        rate, nrows, spent = oracle_rate(run, 3.0, 64, 1 << 16)
+        e["cpu_baseline"] = oracle_entry(
+            rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn rows of the same workload "
+            f"({spent:.1f} s, each call normalising every key row once), fp64")
+    res["tda_fwd B2 H32 T8192 D128 normalised beta=D^-1/2 lambda=0.5 p2 (6D FLOP per pair)"] = e
+    del t5, t5c, ws, out
     # TRA backward at the forward's measured shape
     B, H, T, D = 2, 32, 8192, 128
-    q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
-    do = torch.randn(B, H, T, D, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev)
+    qc, kc, vc = inputs.tra_inputs(B, H, T, D, seed=0)
+    doc = torch.randn(B, H, T, D, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    q, k, v, do = (x.to(dev) for x in (qc, kc, vc, doc))
     g = [torch.empty_like(q) for _ in range(3)]
     fl = 10.0 * D * B * H * T * (T + 1) / 2.0     # five products per pair (S, dP, dV, dK, dQ)
     st = timed(lambda: cat.tra_bwd(q, k, v, do, 1.0, 2.0, dq=g[0], dk=g[1], dv=g[2]), 5, 10, 10)
     tf = fl / (st["ms"] * 1e-3) / 1e12
-    res["tra_bwd B2 H32 T8192 D128 beta1 p2 (10D FLOP per pair)"] = dict(
-        st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
-    del q, k, v, do, g
+    e = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS,
+             roofline=mfma_roofline(fl, st["ms"], f"{fl:.5g} FLOPs (10*D per causal pair)"))
+    if cpu is not None:
+        # n query rows (dq) and n key rows (dk, dv); a row's pairs count 5*D FLOPs on each
+        # side, so that a full pass counts the 10*D per pair above
+        def run(n):
+            qr = rng.integers(0, B * H * T, size=n)
+            kr = rng.integers(0, B * H * T, size=n)
+            t0 = time.perf_counter()
+            oracle.tra_bwd_ref(qc, kc, vc, doc, 1.0, 2.0, qrows=qr, krows=kr)
+            pairs = float(np.sum(qr % T + 1) + np.sum(T - kr % T))
+            return time.perf_counter() - t0, 5.0 * D * pairs
+        rate, nrows, spent = oracle_rate(run, 3.0, 64, 1 << 15)
+        e["cpu_baseline"] = oracle_entry(
+            rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn query rows (dq) and as many key "
+            f"rows (dk, dv) of the same workload ({spent:.1f} s), fp64")
+    res["tra_bwd B2 H32 T8192 D128 beta1 p2 (10D FLOP per pair)"] = e
+    del q, k, v, do, g, qc, kc, vc, doc
     B, Hq, Hkv, T, D, bs, S = 2, 32, 4, 4096, 128, 64, 16
     qn, kn, vn = (x.to(dev) for x in inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0))
     idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
@@ -344,13 +488,15 @@ def extra_configs(dev, nsa_c5=None, ceilings=None):
     o = torch.empty_like(qn)
     lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
     gb = nsa_gathered_bytes(idx, T, bs, D)
+    fl = nsa_useful_flops(idx, T, bs, D, Hq // Hkv)
     st = timed(lambda: cat.nsa_sel_fwd(qn, kn, vn, gidx, bs, out=o, lse=lse), batch=50)
     res["nsa_sel_fwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"] = dict(
-        st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9)
+        st, gathered_gb=gb / 1e9, gbps=gb / (st["ms"] * 1e-3) / 1e9,
+        roofline=mfma_roofline(fl, st["ms"], f"{fl:.5g} useful FLOPs"))
     res.update(nsa_fsa(dev, qn, kn, vn, gidx, bs, gb,
-                       "nsa_sel_fwd_fsa (block-outer) B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
+                       "nsa_sel_fwd_fsa (block-outer) B2 Hq32 Hkv4 T4096 D128 bs64 S16", fl))
     res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv,
-                       "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"))
+                       "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16", fl))
     del qn, kn, vn, gidx, o, lse
     # which NSA forward to call: both forms at B3 Hq16 T8192 D128 bs64 S16 over G = Hq/Hkv
     # (three batches, so that no launch shape coincides with the configurations above)
@@ -366,19 +512,21 @@ def extra_configs(dev, nsa_c5=None, ceilings=None):
         shape = f"B3 Hq16 Hkv{Hkv} (G={Hq // Hkv}) T8192 D128 bs64 S16"
         res[f"nsa_sel_fwd {shape}"] = dict(st, gathered_gb=gb / 1e9,
                                            gbps=gb / (st["ms"] * 1e-3) / 1e9)
-        fsa = nsa_fsa(dev, qn, kn, vn, gidx, bs, gb, f"nsa_sel_fwd_fsa (block-outer) {shape}")
+        fsa = nsa_fsa(dev, qn, kn, vn, gidx, bs, gb, f"nsa_sel_fwd_fsa (block-outer) {shape}",
+                      nsa_useful_flops(idx, T, bs, D, Hq // Hkv))
         for v in fsa.values():
             v["query_outer_ms"] = st["ms"]
             v["speedup_over_query_outer"] = st["ms"] / v["ms"]
         res.update(fsa)
         del qn, kn, vn, gidx, o, lse
     if nsa_c5 is not None:
-        fn, gb, t5 = nsa_c5
-        res.update(nsa_fsa(dev, *t5[:5], gb,
-                           "nsa_sel_fwd_fsa (block-outer) B1 Hq64 Hkv4 T32768 D128 bs64 S16",
-                           3, 5, 5))
-        res.update(nsa_bwd(dev, *t5, gb, NSA["Hq"] // NSA["Hkv"],
-                           "nsa_sel_bwd B1 Hq64 Hkv4 T32768 D128 bs64 S16", 3, 5, 5))
+        fn, gb, t5, fl = nsa_c5
+        kfsa = "nsa_sel_fwd_fsa (block-outer) B1 Hq64 Hkv4 T32768 D128 bs64 S16"
+        kbwd = "nsa_sel_bwd B1 Hq64 Hkv4 T32768 D128 bs64 S16"
+        res.update(nsa_fsa(dev, *t5[:5], gb, kfsa, fl, 3, 5, 5))
+        res.update(nsa_bwd(dev, *t5, gb, NSA["Hq"] // NSA["Hkv"], kbwd, fl, 3, 5, 5))
+        if cpu:
+            nsa_oracle_rates(cpu, res[kfsa], res[kbwd], rng)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         st = stats(time_launches(fn, 2, 8, between=lambda: flush.fill_(1)))
         res["nsa_sel_fwd B1 Hq64 Hkv4 T32768 D128 bs64 S16, cold (512 MiB written before each launch)"] = dict(
@@ -580,8 +728,9 @@ def main():
     if not args.no_extra and args.only is None:
         print("bench: other configurations", file=sys.stderr, flush=True)
         c5 = (lambda: cat.nsa_sel_fwd(gqn, gkn, gvn, gidx, NSA["block_size"], out=o_n, lse=lse_n),
-              gbytes, (gqn, gkn, gvn, gidx, NSA["block_size"], o_n, lse_n))
-        result["other_configs"] = extra_configs(dev, nsa_c5=c5, ceilings=ceilings)
+              gbytes, (gqn, gkn, gvn, gidx, NSA["block_size"], o_n, lse_n), nsa_flops)
+        cpu = None if args.no_cpu_baseline else dict(q=qn, k=kn, v=vn, idx=idx_np)
+        result["other_configs"] = extra_configs(dev, nsa_c5=c5, ceilings=ceilings, cpu=cpu)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(q, k, v, idx_np)

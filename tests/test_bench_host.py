@@ -59,3 +59,30 @@ def test_comment_edits_keep_the_hash(tmp_path, monkeypatch):
     assert b.kernel_source_hash("probe") == h0
     (csrc / "k.hip").write_text("int f() { return 2; }\n")
     assert b.kernel_source_hash("probe") != h0
+
+
+def test_nsa_pair_counts_agree_from_both_sides():
+    """The work counts of the NSA rows: the attended tokens of every query row, summed, equal
+    the attending (query head, query) pairs of every key row over G; per-row counts match
+    a direct count on a tiny case with duplicates, padding, ids past the end and a block
+    after the query."""
+    import numpy as np
+    b = _bench()
+    T, bs, G = 12, 4, 3
+    idx = np.full((1, 2, T, 3), -1, dtype=np.int32)
+    rng = np.random.default_rng(5)
+    for kv in range(2):
+        for i in range(T):
+            idx[0, kv, i] = rng.integers(-1, T // bs + 1, size=3)
+    idx[0, 0, 5] = [1, 1, 2]                  # duplicate, and block 2 starts after query 5
+    direct = []
+    for kv in range(2):
+        for i in range(T):
+            blocks = {int(x) for x in idx[0, kv, i] if 0 <= x < T // bs}
+            direct.append(sum(1 for j in range(i + 1) if j // bs in blocks))
+    tokens = b.nsa_tokens(idx, T, bs)
+    assert tokens.tolist() == direct
+    assert b.nsa_tokens(idx, T, bs, [5, 17]).tolist() == [direct[5], direct[17]]
+    assert b.nsa_useful_flops(idx, T, bs, 64, G) == 4.0 * 64 * G * sum(direct)
+    keys = b.nsa_key_pairs(idx, T, bs, G, np.arange(2 * T))
+    assert keys.sum() == G * sum(direct)
