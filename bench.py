@@ -377,9 +377,10 @@ def nsa_oracle_rates(cpu, fsa_entry, bwd_entry, rng, budget_s=3.0):
         s = time.perf_counter() - t0
         pairs = float(nsa_tokens(idx, T, bs, kv_rows(qr)).sum() + nsa_key_pairs(idx, T, bs, G, kr).sum())
         return s, 5.0 * D * pairs
-    # the oracle's key rows recompute the softmax statistics of every attending query row,
-    # so they cost far more than their pairs: small first samples
-    rate, nrows, spent = oracle_rate(bwd, budget_s, 32, 1 << 16)
+    # the oracle's key rows recompute the softmax statistics of every attending query row
+    # (seconds per key row at this length); the oracle runs rows in parallel, so the first
+    # sample holds 16 key rows, one per host thread
+    rate, nrows, spent = oracle_rate(bwd, budget_s, 256, 1 << 16)
     bwd_entry["cpu_baseline"] = oracle_entry(
         rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn (head, query) rows (dq) and "
         f"{Hkv}/{Hq} as many (kv head, key) rows (dk, dv) of the same workload ({spent:.1f} s), fp64")
