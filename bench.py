@@ -105,18 +105,6 @@ def nsa_useful_flops(idx, T, bs, D, G):
     return 4.0 * D * G * float(nsa_tokens(idx, T, bs).sum())
 
 
-def nsa_key_pairs(idx, T, bs, G, krows):
-    """(query head, query) pairs that attend each key row (flat (b*Hkv+kv)*T+j ids): G for
-    every query i >= j whose selection holds the key's block."""
-    Hkv = idx.shape[1]
-    out = np.empty(len(krows))
-    for n, r in enumerate(np.asarray(krows)):
-        bk, j = divmod(int(r), T)
-        b, kv = divmod(bk, Hkv)
-        out[n] = G * np.count_nonzero((idx[b, kv, j:, :] == j // bs).any(axis=1))
-    return out
-
-
 def mfma_roofline(flops, ms, note):
     """Roofline entry of a kernel bound by the bf16 matrix units: useful FLOPs per launch
     over the launch time against the published dense peak."""
@@ -342,12 +330,10 @@ def nsa_fsa(dev, q, k, v, gidx, bs, gb, what, flops, warm=5, per_launch=10, batc
                        roofline=roof)}
 
 
-def nsa_oracle_rates(cpu, fsa_entry, bwd_entry, rng, budget_s=3.0):
-    """The oracle on bounded samples of the headline NSA workload (B1 Hq64 Hkv4 T32768 G16),
-    in useful TFLOP/s: the forward (which the block-outer form computes too) at 4*D per
-    (query head, attended token), and the backward at 10*D per pair, counted 5*D on the
-    dq side for each sampled query row's pairs and 5*D on the dk/dv side for each sampled
-    key row's pairs (key rows drawn at the same fraction of all key rows)."""
+def nsa_fwd_oracle_rate(cpu, fsa_entry, rng, budget_s=3.0):
+    """The forward oracle (the function the block-outer form computes too) on bounded
+    samples of the headline NSA workload (B1 Hq64 Hkv4 T32768 G16), in useful TFLOP/s at
+    4*D per (query head, attended token)."""
     import oracle
     q, k, v, idx = cpu["q"], cpu["k"], cpu["v"], cpu["idx"]
     B, Hq, T, D = q.shape
@@ -367,23 +353,6 @@ def nsa_oracle_rates(cpu, fsa_entry, bwd_entry, rng, budget_s=3.0):
     fsa_entry["cpu_baseline"] = oracle_entry(
         rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn (head, query) rows of the same "
         f"workload through the forward oracle ({spent:.1f} s), fp64")
-    dout = torch.randn(*q.shape, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
-
-    def bwd(n):
-        qr = rng.integers(0, B * Hq * T, size=n)
-        kr = rng.integers(0, B * Hkv * T, size=max(1, n * Hkv // Hq))
-        t0 = time.perf_counter()
-        oracle.nsa_bwd_ref(q, k, v, idx, bs, dout, qrows=qr, krows=kr)
-        s = time.perf_counter() - t0
-        pairs = float(nsa_tokens(idx, T, bs, kv_rows(qr)).sum() + nsa_key_pairs(idx, T, bs, G, kr).sum())
-        return s, 5.0 * D * pairs
-    # the oracle's key rows recompute the softmax statistics of every attending query row
-    # (seconds per key row at this length); the oracle runs rows in parallel, so the first
-    # sample holds 16 key rows, one per host thread
-    rate, nrows, spent = oracle_rate(bwd, budget_s, 256, 1 << 16)
-    bwd_entry["cpu_baseline"] = oracle_entry(
-        rate / 1e12, "TFLOP/s", f"{nrows} uniformly drawn (head, query) rows (dq) and "
-        f"{Hkv}/{Hq} as many (kv head, key) rows (dk, dv) of the same workload ({spent:.1f} s), fp64")
 
 
 def tra_evaluated_weights(B, H, T, rows_per_wave=32, keys_per_tile=64):
@@ -483,7 +452,8 @@ def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
     res["tra_bwd B2 H32 T8192 D128 beta1 p2 (10D FLOP per pair)"] = e
     del q, k, v, do, g, qc, kc, vc, doc
     B, Hq, Hkv, T, D, bs, S = 2, 32, 4, 4096, 128, 64, 16
-    qn, kn, vn = (x.to(dev) for x in inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0))
+    nsa_c4 = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=0)
+    qn, kn, vn = (x.to(dev) for x in nsa_c4)
     idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=0)
     gidx = torch.from_numpy(idx).to(dev)
     o = torch.empty_like(qn)
@@ -496,9 +466,20 @@ def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
         roofline=mfma_roofline(fl, st["ms"], f"{fl:.5g} useful FLOPs"))
     res.update(nsa_fsa(dev, qn, kn, vn, gidx, bs, gb,
                        "nsa_sel_fwd_fsa (block-outer) B2 Hq32 Hkv4 T4096 D128 bs64 S16", fl))
-    res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv,
-                       "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16", fl))
-    del qn, kn, vn, gidx, o, lse
+    kbwd = "nsa_sel_bwd B2 Hq32 Hkv4 T4096 D128 bs64 S16"
+    res.update(nsa_bwd(dev, qn, kn, vn, gidx, bs, o, lse, gb, Hq // Hkv, kbwd, fl))
+    if cpu is not None:
+        # one call over every row: each call of the backward oracle first computes the
+        # softmax statistics of every query row, which a sample of rows would not amortise
+        doc = torch.randn(B, Hq, T, D, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+        t0 = time.perf_counter()
+        oracle.nsa_bwd_ref(*nsa_c4, idx, bs, doc)
+        spent = time.perf_counter() - t0
+        res[kbwd]["cpu_baseline"] = oracle_entry(
+            2.5 * fl / spent / 1e12, "TFLOP/s", f"the whole workload (every dq, dk and dv row) "
+            f"in one call ({spent:.1f} s), fp64")
+        del doc
+    del qn, kn, vn, gidx, o, lse, nsa_c4
     # which NSA forward to call: both forms at B3 Hq16 T8192 D128 bs64 S16 over G = Hq/Hkv
     # (three batches, so that no launch shape coincides with the configurations above)
     B, Hq, T, D, bs, S = 3, 16, 8192, 128, 64, 16
@@ -527,7 +508,7 @@ def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
         res.update(nsa_fsa(dev, *t5[:5], gb, kfsa, fl, 3, 5, 5))
         res.update(nsa_bwd(dev, *t5, gb, NSA["Hq"] // NSA["Hkv"], kbwd, fl, 3, 5, 5))
         if cpu:
-            nsa_oracle_rates(cpu, res[kfsa], res[kbwd], rng)
+            nsa_fwd_oracle_rate(cpu, res[kfsa], rng)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         st = stats(time_launches(fn, 2, 8, between=lambda: flush.fill_(1)))
         res["nsa_sel_fwd B1 Hq64 Hkv4 T32768 D128 bs64 S16, cold (512 MiB written before each launch)"] = dict(

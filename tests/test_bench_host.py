@@ -61,11 +61,10 @@ def test_comment_edits_keep_the_hash(tmp_path, monkeypatch):
     assert b.kernel_source_hash("probe") != h0
 
 
-def test_nsa_pair_counts_agree_from_both_sides():
-    """The work counts of the NSA rows: the attended tokens of every query row, summed, equal
-    the attending (query head, query) pairs of every key row over G; per-row counts match
-    a direct count on a tiny case with duplicates, padding, ids past the end and a block
-    after the query."""
+def test_nsa_token_counts():
+    """The work counts of the NSA rows: the attended tokens of each query row match a direct
+    count on a tiny case with duplicates, padding, ids past the end and a block after the
+    query, for all rows and for a subset."""
     import numpy as np
     b = _bench()
     T, bs, G = 12, 4, 3
@@ -84,5 +83,3 @@ def test_nsa_pair_counts_agree_from_both_sides():
     assert tokens.tolist() == direct
     assert b.nsa_tokens(idx, T, bs, [5, 17]).tolist() == [direct[5], direct[17]]
     assert b.nsa_useful_flops(idx, T, bs, 64, G) == 4.0 * 64 * G * sum(direct)
-    keys = b.nsa_key_pairs(idx, T, bs, G, np.arange(2 * T))
-    assert keys.sum() == G * sum(direct)
