@@ -375,7 +375,8 @@ def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
     carry a roofline entry; with cpu (the headline NSA inputs on the host, or {} to skip
     the NSA rows) each also carries the oracle timed on a bounded sample of its rows, in
     the same unit."""
-    import oracle
+    if cpu is not None:
+        import oracle  # the cpu_baseline entries only
     rng = np.random.default_rng(77)
     res = {}
     B, H, T, D = 4, 16, 2048, 64
