@@ -60,6 +60,18 @@ def test_tda_config_T8192_D128_all_rows(gpu):
     assert_rows_close(out, ref, BF16_REL, "tda T8192")
 
 
+def test_tda_long_T32768_sampled_rows(gpu):
+    """Normalised, B=1 H=1 T=32768 D=128, beta=D^-1/2, lambda=0.5, p=2: the first rows, one
+    row in 512 and the last 64 rows against the oracle."""
+    T, D = 32768, 128
+    print("tda T32768", flush=True)
+    t5 = inputs.tda_inputs(1, 1, T, D, seed=14)
+    out = _run(t5, D ** -0.5, 0.5, 2.0, True, gpu).reshape(-1, D)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(7, T, 512), np.arange(T - 64, T)]))
+    ref = oracle.tda_ref(*t5, D ** -0.5, 0.5, 2.0, normalize=True, rows=rows)
+    assert_rows_close(out[rows], ref, BF16_REL, "tda T32768")
+
+
 @pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
 def test_tda_lambda_zero_matches_tra(gpu, p, D):

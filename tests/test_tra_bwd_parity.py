@@ -1,6 +1,7 @@
 """GPU parity of the Threshold Rectified Attention backward (tra_bwd) against the
 fp64 oracle on the same seeded inputs, plus GPU-only properties that must hold bit
 for bit (determinism, causal dependency structure)."""
+import numpy as np
 import pytest
 import torch
 
@@ -100,6 +101,22 @@ def test_tra_bwd_T2048_D64_all_rows(gpu, p):
     assert_rows_close(dq, rq, BF16_REL, f"dq T2048 D64 p={p}")
     assert_rows_close(dk, rk, BF16_REL, f"dk T2048 D64 p={p}")
     assert_rows_close(dv, rv, BF16_REL, f"dv T2048 D64 p={p}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_tra_bwd_long_T65536_sampled_rows(gpu, D):
+    """B=1 H=1 T=65536 (256 key workgroups at D=128, 512 at D=64): dq on the first rows,
+    one row in 512 and the last 64, dk and dv on the same key rows, against the oracle."""
+    T = 65536
+    print(f"tra_bwd T65536 D{D}", flush=True)
+    q, k, v = inputs.tra_inputs(1, 1, T, D, seed=12)
+    do = _dout(1, 1, T, D, seed=13)
+    dq, dk, dv = _run(q, k, v, do, 1.0, 2.0, gpu)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(7, T, 512), np.arange(T - 64, T)]))
+    rq, rk, rv = oracle.tra_bwd_ref(q, k, v, do, 1.0, 2.0, qrows=rows, krows=rows)
+    assert_rows_close(dq.reshape(-1, D)[rows], rq, BF16_REL, f"dq T65536 D{D}")
+    assert_rows_close(dk.reshape(-1, D)[rows], rk, BF16_REL, f"dk T65536 D{D}")
+    assert_rows_close(dv.reshape(-1, D)[rows], rv, BF16_REL, f"dv T65536 D{D}")
 
 
 def test_tra_bwd_deterministic(gpu):

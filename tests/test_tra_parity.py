@@ -93,6 +93,24 @@ def test_tra_config_bf16_T2048_D64(gpu, p):
     assert_rows_close(out, ref, BF16_REL, f"T2048 p={p}")
 
 
+def _long_rows(T):
+    """Rows of one head at a long sequence: the first four, one in 512, and the last 64."""
+    return np.unique(np.concatenate([np.arange(4), np.arange(7, T, 512), np.arange(T - 64, T)]))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_tra_long_T65536_sampled_rows(gpu, D):
+    """bf16, B=1 H=1 T=65536 (1024 key tiles): the first rows, one row in 512 and the last
+    64 rows against the oracle."""
+    T = 65536
+    print(f"tra T65536 D{D}", flush=True)
+    q, k, v = inputs.tra_inputs(1, 1, T, D, seed=11)
+    out = _run_bf16(q, k, v, 1.0, 2.0, gpu).reshape(-1, D)
+    rows = _long_rows(T)
+    ref = oracle.tra_ref(q, k, v, 1.0, 2.0, rows=rows)
+    assert_rows_close(out[rows], ref, BF16_REL, f"T65536 D{D}")
+
+
 @pytest.fixture(scope="module")
 def big_tra():
     c = inputs.CONFIGS["tra_bf16_T8192_D128"]
