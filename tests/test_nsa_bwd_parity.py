@@ -186,3 +186,24 @@ def test_nsa_bwd_T32768_G16_dense_slice(gpu):
                       floor=FLOOR, floor_rows=one)
     assert_rows_close(dk.reshape(-1, D)[krows], rk, BF16_REL, "dk T32768")
     assert_rows_close(dv.reshape(-1, D)[krows], rv, BF16_REL, "dv T32768")
+
+
+def test_nsa_bwd_long_T131072_G16_sampled_rows(gpu):
+    """B=1 Hq=16 Hkv=1 T=131072 D=128 bs=64 S=16 (2048 blocks): dq on every head at the
+    first four query positions, one in 512 and the last 64; dk and dv at one key position
+    in 64 (and 0, 63, 64, T-1), against the oracle in one call."""
+    B, Hq, Hkv, T, D, bs, S = 1, 16, 1, 131072, 128, 64, 16
+    print("nsa_bwd T131072: inputs", flush=True)
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=22)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=22)
+    do = _dout((B, Hq, T, D), seed=23)
+    dq, dk, dv = _run(q, k, v, idx, bs, do, gpu)
+    qrows = _strided_rows(B * Hq, T, 512, 7, (0, 1, 2, 3) + tuple(range(T - 64, T)))
+    krows = _strided_rows(B * Hkv, T, 64, 3, (0, 63, 64, T - 1))
+    print(f"nsa_bwd T131072: oracle on {qrows.size} dq rows, {krows.size} dk/dv rows", flush=True)
+    rq, rk, rv = oracle.nsa_bwd_ref(q, k, v, idx, bs, do, qrows=qrows, krows=krows)
+    one = _single_key_rows(idx, bs, Hq // Hkv).reshape(-1)[qrows]
+    assert_rows_close(dq.reshape(-1, D)[qrows], rq, BF16_REL, "dq T131072",
+                      floor=FLOOR, floor_rows=one)
+    assert_rows_close(dk.reshape(-1, D)[krows], rk, BF16_REL, "dk T131072")
+    assert_rows_close(dv.reshape(-1, D)[krows], rv, BF16_REL, "dv T131072")

@@ -174,3 +174,21 @@ def test_nsa_config_T32768_G16(gpu, nsa_c5_case):
     assert_rows_close(o.reshape(-1, D)[c["rows"]], c["ref_o"], BF16_REL, "T32768 G16")
     assert_lse_close(lse.reshape(-1)[c["rows"]], c["ref_lse"], "T32768 G16")
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_nsa_long_T131072_G16_sampled_rows(gpu):
+    """B=1 Hq=16 Hkv=1 T=131072 D=128 bs=64 S=16 (2048 blocks): o and lse of both forwards
+    on every head at the first four query positions, one in 512 and the last 64."""
+    import test_nsa_fsa_parity as fsa
+    B, Hq, Hkv, T, D, bs, S = 1, 16, 1, 131072, 128, 64, 16
+    print("nsa T131072: inputs", flush=True)
+    q, k, v = inputs.nsa_inputs(B, Hq, Hkv, T, D, seed=21)
+    idx = inputs.nsa_block_idx(B, Hkv, T, bs, S, seed=21)
+    pos = np.unique(np.concatenate([np.arange(4), np.arange(7, T, 512), np.arange(T - 64, T)]))
+    rows = (np.arange(B * Hq)[:, None] * T + pos[None, :]).reshape(-1)
+    ro, rl = oracle.nsa_ref(q, k, v, idx, bs, rows=rows)
+    for name, run in (("query-outer", _run), ("block-outer", fsa._run)):
+        print(f"nsa T131072: {name}", flush=True)
+        o, lse = run(q, k, v, idx, bs, gpu)
+        assert_rows_close(o.reshape(-1, D)[rows], ro, BF16_REL, f"nsa T131072 {name}")
+        assert_lse_close(lse.reshape(-1)[rows], rl, f"nsa T131072 {name}")
