@@ -8,7 +8,14 @@
 
 namespace attn {
 
-enum PowMode { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2 };
+// kPowThreeHalves: p = 1.5 exactly, max(x, 0)^1.5 = r * sqrt(r) with one square root
+// instead of a log and an exp (the same value up to rounding).
+enum PowMode { kPowGeneral = 0, kPowOne = 1, kPowTwo = 2, kPowThreeHalves = 3 };
+
+// The kernel instantiation for a power p: exact forms for p = 1, 2 and 1.5, else exp2/log2.
+inline int pow_mode(float p) {
+    return p == 1.0f ? kPowOne : p == 2.0f ? kPowTwo : p == 1.5f ? kPowThreeHalves : kPowGeneral;
+}
 
 template <int PM>
 __device__ __forceinline__ float relu_pow(float x, float p) {
@@ -17,6 +24,9 @@ __device__ __forceinline__ float relu_pow(float x, float p) {
     } else if constexpr (PM == kPowTwo) {
         const float r = fmaxf(x, 0.0f);
         return r * r;
+    } else if constexpr (PM == kPowThreeHalves) {
+        const float r = fmaxf(x, 0.0f);
+        return r * __builtin_amdgcn_sqrtf(r);
     } else {
         // x^p = 2^(p log2 x) for x > 0 (v_log_f32 / v_exp_f32 are base 2).  For x <= 0
         // (and the -inf of masked keys) max(x, 0) = 0, log2(0) = -inf and, as p > 0,

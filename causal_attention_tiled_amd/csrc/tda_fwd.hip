@@ -356,9 +356,11 @@ hipError_t launch_d(const uint16_t *q1, const uint16_t *q2, const uint16_t *k1,
         k1 = y0;
         k2 = y1;
     }
-    const int pm = p == 1.0f ? kPowOne : (p == 2.0f ? kPowTwo : kPowGeneral);
+    const int pm = pow_mode(p);
     if (pm == kPowTwo) return launch_main<D, kPowTwo>(q1, q2, k1, k2, v, out, BH, T, beta, lam, p, normalize, stream);
     if (pm == kPowOne) return launch_main<D, kPowOne>(q1, q2, k1, k2, v, out, BH, T, beta, lam, p, normalize, stream);
+    if (pm == kPowThreeHalves)
+        return launch_main<D, kPowThreeHalves>(q1, q2, k1, k2, v, out, BH, T, beta, lam, p, normalize, stream);
     return launch_main<D, kPowGeneral>(q1, q2, k1, k2, v, out, BH, T, beta, lam, p, normalize, stream);
 }
 

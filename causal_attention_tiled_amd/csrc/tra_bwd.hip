@@ -56,6 +56,8 @@ __device__ __forceinline__ float relu_pow_m1(float x, float p) {
         return x > 0.0f ? 1.0f : 0.0f;
     } else if constexpr (PM == kPowTwo) {
         return fmaxf(x, 0.0f);
+    } else if constexpr (PM == kPowThreeHalves) {
+        return __builtin_amdgcn_sqrtf(fmaxf(x, 0.0f));
     } else {
         return x > 0.0f ? __builtin_amdgcn_exp2f((p - 1.0f) * __builtin_amdgcn_logf(x)) : 0.0f;
     }
@@ -70,6 +72,10 @@ __device__ __forceinline__ void relu_pow_both(float x, float p, float &w, float 
         const float l = __builtin_amdgcn_logf(fmaxf(x, 0.0f));
         w = __builtin_amdgcn_exp2f(p * l);
         g = x > 0.0f ? __builtin_amdgcn_exp2f((p - 1.0f) * l) : 0.0f;
+    } else if constexpr (PM == kPowThreeHalves) {
+        const float r = fmaxf(x, 0.0f);
+        g = __builtin_amdgcn_sqrtf(r);
+        w = r * g;
     } else {
         w = relu_pow<PM>(x, p);
         g = relu_pow_m1<PM>(x, p);
@@ -881,14 +887,18 @@ hipError_t launch(const uint16_t *q, const uint16_t *k, const uint16_t *v, const
 hipError_t launch_tra_bwd_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const uint16_t *dout, uint16_t *dq, uint16_t *dk, uint16_t *dv,
                                int BH, int T, int D, float beta, float p, hipStream_t stream) {
-    const int pm = p == 1.0f ? kPowOne : (p == 2.0f ? kPowTwo : kPowGeneral);
+    const int pm = pow_mode(p);
     if (D == 128) {
         if (pm == kPowTwo) return launch<128, kPowTwo>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
         if (pm == kPowOne) return launch<128, kPowOne>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+        if (pm == kPowThreeHalves)
+            return launch<128, kPowThreeHalves>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
         return launch<128, kPowGeneral>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
     }
     if (pm == kPowTwo) return launch<64, kPowTwo>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
     if (pm == kPowOne) return launch<64, kPowOne>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
+    if (pm == kPowThreeHalves)
+        return launch<64, kPowThreeHalves>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
     return launch<64, kPowGeneral>(q, k, v, dout, dq, dk, dv, BH, T, beta, p, stream);
 }
 

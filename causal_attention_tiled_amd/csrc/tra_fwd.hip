@@ -485,7 +485,6 @@ hipError_t launch_f32(const float *q, const float *k, const float *v, float *out
                            dim3((unsigned)(BH * nqt)), dim3(kThreads), args, 0, stream);
 }
 
-int pow_mode(float p) { return p == 1.0f ? kPowOne : (p == 2.0f ? kPowTwo : kPowGeneral); }
 
 }  // namespace
 
@@ -496,10 +495,12 @@ hipError_t launch_tra_fwd_bf16(const uint16_t *q, const uint16_t *k, const uint1
     if (D == 128) {
         if (pm == kPowTwo) return launch_bf16<128, kPowTwo>(q, k, v, out, BH, T, beta, p, stream);
         if (pm == kPowOne) return launch_bf16<128, kPowOne>(q, k, v, out, BH, T, beta, p, stream);
+        if (pm == kPowThreeHalves) return launch_bf16<128, kPowThreeHalves>(q, k, v, out, BH, T, beta, p, stream);
         return launch_bf16<128, kPowGeneral>(q, k, v, out, BH, T, beta, p, stream);
     }
     if (pm == kPowTwo) return launch_bf16<64, kPowTwo>(q, k, v, out, BH, T, beta, p, stream);
     if (pm == kPowOne) return launch_bf16<64, kPowOne>(q, k, v, out, BH, T, beta, p, stream);
+    if (pm == kPowThreeHalves) return launch_bf16<64, kPowThreeHalves>(q, k, v, out, BH, T, beta, p, stream);
     return launch_bf16<64, kPowGeneral>(q, k, v, out, BH, T, beta, p, stream);
 }
 
@@ -509,10 +510,12 @@ hipError_t launch_tra_fwd_f32(const float *q, const float *k, const float *v, fl
     if (D == 128) {
         if (pm == kPowTwo) return launch_f32<128, kPowTwo>(q, k, v, out, BH, T, beta, p, stream);
         if (pm == kPowOne) return launch_f32<128, kPowOne>(q, k, v, out, BH, T, beta, p, stream);
+        if (pm == kPowThreeHalves) return launch_f32<128, kPowThreeHalves>(q, k, v, out, BH, T, beta, p, stream);
         return launch_f32<128, kPowGeneral>(q, k, v, out, BH, T, beta, p, stream);
     }
     if (pm == kPowTwo) return launch_f32<64, kPowTwo>(q, k, v, out, BH, T, beta, p, stream);
     if (pm == kPowOne) return launch_f32<64, kPowOne>(q, k, v, out, BH, T, beta, p, stream);
+    if (pm == kPowThreeHalves) return launch_f32<64, kPowThreeHalves>(q, k, v, out, BH, T, beta, p, stream);
     return launch_f32<64, kPowGeneral>(q, k, v, out, BH, T, beta, p, stream);
 }
 

@@ -32,7 +32,7 @@ def test_tra_random(gpu, seed):
     rng = np.random.default_rng(seed)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
     T, D = int(rng.integers(1, 700)), _pick(rng, [64, 128])
-    p = _pick(rng, [1.0, 2.0, 1.5, 0.5, 3.0])
+    p = _pick(rng, [1.0, 2.0, 1.5, 1.25, 0.5, 3.0])
     beta = float(rng.uniform(-0.5, 1.5))
     print(f"tra B{B} H{H} T{T} D{D} p{p} beta{beta:.3f}", flush=True)
     q, k, v = inputs.tra_inputs(B, H, T, D, seed=int(seed % 1000))
@@ -46,7 +46,7 @@ def test_tra_f32_random(gpu, seed):
     rng = np.random.default_rng(seed)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
     T, D = int(rng.integers(1, 320)), _pick(rng, [64, 128])
-    p = _pick(rng, [1.0, 2.0, 1.5])
+    p = _pick(rng, [1.0, 2.0, 1.5, 1.25])
     beta = float(rng.uniform(-0.5, 1.5))
     print(f"tra f32 B{B} H{H} T{T} D{D} p{p} beta{beta:.3f}", flush=True)
     q, k, v = inputs.tra_inputs(B, H, T, D, dtype=torch.float32, seed=int(seed % 1000))
@@ -60,7 +60,7 @@ def test_tra_bwd_random(gpu, seed):
     rng = np.random.default_rng(seed)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
     T, D = int(rng.integers(1, 420)), _pick(rng, [64, 128])
-    p = _pick(rng, [1.0, 2.0, 1.5, 3.0])
+    p = _pick(rng, [1.0, 2.0, 1.5, 1.25, 3.0])
     beta = float(rng.uniform(-0.5, 1.5))
     print(f"tra_bwd B{B} H{H} T{T} D{D} p{p} beta{beta:.3f}", flush=True)
     q, k, v = inputs.tra_inputs(B, H, T, D, seed=int(seed % 1000))
@@ -77,7 +77,7 @@ def test_tda_random(gpu, seed):
     rng = np.random.default_rng(seed)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
     T, D = int(rng.integers(1, 420)), _pick(rng, [64, 128])
-    p = _pick(rng, [1.0, 2.0, 1.5])
+    p = _pick(rng, [1.0, 2.0, 1.5, 1.25])
     norm = bool(rng.integers(0, 2))
     beta = float(rng.uniform(-0.05, 0.15)) if norm else float(rng.uniform(-0.5, 1.5))
     lam = float(rng.uniform(-0.3, 1.3))

@@ -27,7 +27,7 @@ SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 1, 129, 64), (1, 2
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
 @pytest.mark.parametrize("normalize", [True, False], ids=["norm", "raw"])
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tda_small(gpu, shape, normalize, p):
     B, H, T, D = shape
     print(f"tda {shape} normalize={normalize} p={p}", flush=True)
@@ -73,7 +73,7 @@ def test_tda_long_T32768_sampled_rows(gpu):
 
 
 @pytest.mark.parametrize("D", [128, 64])
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tda_lambda_zero_matches_tra(gpu, p, D):
     """lambda = 0, no normalisation: the output is the rectified forward of path 1, bit
     for bit (both kernels start the scores at -tau, accumulate the same products in the

@@ -34,7 +34,7 @@ SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 1, 129, 64), (1, 2
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tra_bwd_small(gpu, shape, p):
     B, H, T, D = shape
     print(f"tra_bwd {shape} p={p}", flush=True)
@@ -117,6 +117,19 @@ def test_tra_bwd_long_T65536_sampled_rows(gpu, D):
     assert_rows_close(dq.reshape(-1, D)[rows], rq, BF16_REL, f"dq T65536 D{D}")
     assert_rows_close(dk.reshape(-1, D)[rows], rk, BF16_REL, f"dk T65536 D{D}")
     assert_rows_close(dv.reshape(-1, D)[rows], rv, BF16_REL, f"dv T65536 D{D}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_tra_bwd_general_p_path_matches_three_halves_path(gpu, D):
+    """p = the next fp32 above 1.5 (exp2/log2 of one shared log) against p = 1.5 (one
+    square root for the weight and its derivative): within tolerance."""
+    p_next = float(np.nextafter(np.float32(1.5), np.float32(2.0)))
+    q, k, v = inputs.tra_inputs(1, 2, 300, D, seed=9)
+    do = _dout(1, 2, 300, D, seed=10)
+    a = _run(q, k, v, do, 1.0, 1.5, gpu)
+    b = _run(q, k, v, do, 1.0, p_next, gpu)
+    for x, y, n in zip(b, a, ("dq", "dk", "dv")):
+        assert_rows_close(x, y.double().numpy(), BF16_REL, f"{n} general-p vs p=1.5")
 
 
 def test_tra_bwd_deterministic(gpu):

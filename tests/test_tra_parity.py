@@ -34,7 +34,7 @@ SMALL = [(1, 2, 1, 128), (1, 2, 63, 64), (2, 1, 65, 128), (1, 3, 127, 64), (1, 1
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dT%dD%d" % s)
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tra_bf16_small(gpu, shape, p):
     B, H, T, D = shape
     print(f"tra bf16 {shape} p={p}", flush=True)
@@ -57,7 +57,7 @@ def test_tra_bf16_beta_p(gpu, beta, p):
 
 @pytest.mark.parametrize("shape", [(1, 2, 1, 64), (1, 2, 63, 128), (2, 1, 65, 64), (1, 2, 200, 128)],
                          ids=lambda s: "B%dH%dT%dD%d" % s)
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tra_f32_small(gpu, shape, p):
     B, H, T, D = shape
     q, k, v = inputs.tra_inputs(B, H, T, D, dtype=torch.float32, seed=T)
@@ -81,7 +81,7 @@ def test_tra_f32_T1024_D128(gpu, p):
     assert_rows_close(out, oracle.tra_ref(q, k, v, 1.0, p), F32_REL, f"f32 T1024 D128 p={p}")
 
 
-@pytest.mark.parametrize("p", [1.0, 2.0, 1.5])
+@pytest.mark.parametrize("p", [1.0, 2.0, 1.5, 1.25])
 def test_tra_config_bf16_T2048_D64(gpu, p):
     """bf16, B=4 H=16 T=2048 D=64, beta=1, p in {1, 2, 1.5}: every element."""
     c = inputs.CONFIGS["tra_bf16_T2048_D64"]
@@ -168,6 +168,21 @@ def test_tra_general_p_path_matches_fast_path(gpu):
     a = _run_bf16(q, k, v, 1.0, 2.0, gpu)
     b = _run_bf16(q, k, v, 1.0, p_next, gpu)
     assert_rows_close(b, a.double().numpy(), BF16_REL, "general-p vs p=2")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_tra_general_p_path_matches_three_halves_path(gpu, D):
+    """p = the next fp32 above 1.5 takes the exp2/log2 path, p = 1.5 the r*sqrt(r) one:
+    within tolerance of each other, bf16 and fp32."""
+    p_next = float(np.nextafter(np.float32(1.5), np.float32(2.0)))
+    q, k, v = inputs.tra_inputs(1, 2, 300, D, dtype=torch.bfloat16, seed=8)
+    a = _run_bf16(q, k, v, 1.0, 1.5, gpu)
+    b = _run_bf16(q, k, v, 1.0, p_next, gpu)
+    assert_rows_close(b, a.double().numpy(), BF16_REL, "general-p vs p=1.5, bf16")
+    q, k, v = inputs.tra_inputs(1, 2, 300, D, dtype=torch.float32, seed=8)
+    a = _run_f32(q, k, v, 1.0, 1.5, gpu)
+    b = _run_f32(q, k, v, 1.0, p_next, gpu)
+    assert_rows_close(b, a.double().numpy(), F32_REL, "general-p vs p=1.5, fp32")
 
 
 def test_tra_empty_is_noop(gpu):
