@@ -12,7 +12,7 @@ seeded synthetic batch already resident in HBM:
 W untimed steps, then K timed steps between two device synchronisations.
 Per-launch kernel durations come from HIP events recorded on the stream the
 kernels run on.  After the timed steps, the other configurations of the method
-(TRA at T=2048 D=64 for p = 1, 2, 1.5; TRA fp32 at T=256; Threshold Differential
+(TRA at T=2048 D=64 for p = 1, 2, 1.5, 1.25; TRA fp32 at T=256; Threshold Differential
 Attention at T=8192 D=128; the TRA backward at T=8192 D=128; NSA G=8 at T=4096;
 NSA G=16 at T=32768 with caches flushed before each launch, the NSA backward and
 block-outer forward at both NSA shapes) are timed on their own and reported under
@@ -366,7 +366,7 @@ def tra_evaluated_weights(B, H, T, rows_per_wave=32, keys_per_tile=64):
 
 def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
     """The other workloads of the method at their own sizes (not the headline line):
-    TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5; TRA fp32 B1 H2 T256 D64; TDA bf16
+    TRA bf16 B4 H16 T2048 D64 at p = 1, 2, 1.5, 1.25; TRA fp32 B1 H2 T256 D64; TDA bf16
     B2 H32 T8192 D128 (normalised); the TRA backward at B2 H32 T8192 D128; NSA G=8
     at T=4096 (forward, block-outer forward and backward); both NSA forwards at B3
     Hq16 T8192 for G = 1, 2, 4, 8, 16; and NSA G=16 at T=32768:
@@ -383,13 +383,14 @@ def extra_configs(dev, nsa_c5=None, ceilings=None, cpu=None):
     q, k, v = (x.to(dev) for x in inputs.tra_inputs(B, H, T, D, seed=0))
     out = torch.empty_like(q)
     fl = tra_useful_flops(B, H, T, D)
-    for pw in (1.0, 2.0, 1.5):
+    for pw in (1.0, 2.0, 1.5, 1.25):
         st = timed(lambda: cat.tra_fwd(q, k, v, 1.0, pw, out=out), batch=200)
         tf = fl / (st["ms"] * 1e-3) / 1e12
         r = dict(st, tflops=tf, frac_bf16_peak=tf / PEAK_BF16_TFLOPS)
-        if pw == 1.5:
-            # the general power costs one v_log_f32 and one v_exp_f32 per evaluated weight
-            ops = 2.0 * tra_evaluated_weights(B, H, T)
+        if pw in (1.5, 1.25):
+            # p = 1.5 costs one v_sqrt_f32 per evaluated weight, the general power one
+            # v_log_f32 and one v_exp_f32 (transcendental-unit operations alike)
+            ops = (1.0 if pw == 1.5 else 2.0) * tra_evaluated_weights(B, H, T)
             r["transcendental_ops"] = ops
             r["transcendental_ops_per_s"] = ops / (st["ms"] * 1e-3)
             if ceilings is not None:
