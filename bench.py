@@ -139,21 +139,33 @@ def nsa_unique_bytes(B, Hq, Hkv, T, D, S):
     return float(2 * B * Hkv * T * D * 2 + 2 * B * Hq * T * D * 2 + B * Hq * T * 4 + B * Hkv * T * S * 4)
 
 
+def build_flags_text(path):
+    """The compile-flag definitions of the build script (ARCH, CXXFLAGS, the per-file extra
+    flags), # comments and blank lines left out: the part of it that decides the code a
+    kernel compiles to."""
+    import re
+    with open(path) as fh:
+        text = fh.read()
+    parts = re.findall(r"^(?:ARCH = [^\n]*$|CXXFLAGS = \[.*?^\]|_THRESHOLD_FLAGS = \[.*?\]$"
+                       r"|EXTRA = \{.*?\}$)", text, re.S | re.M)
+    lines = (re.sub(r"#.*$", "", ln).rstrip() for p in parts for ln in p.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(name):
-    """Hash of the kernel's sources and the build script; in the C/HIP files, // comments
-    and blank lines are left out, so an edit of a comment keeps a measurement valid and
-    any edit of code invalidates it."""
+    """Hash of the kernel's sources and of the build script's compile flags; in the C/HIP
+    files, // comments and blank lines are left out, so an edit of a comment (or of how the
+    build runs its compiles) keeps a measurement valid and any edit of code or flags
+    invalidates it."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[name] + ["../build.py"]:
+    for f in KERNEL_SOURCES[name]:
         with open(os.path.join(CSRC, f), "rb") as fh:
-            data = fh.read()
-        if not f.endswith(".py"):
-            text = data.decode()
-            lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
-            data = "\n".join(ln for ln in lines if ln).encode()
-        h.update(data)
+            text = fh.read().decode()
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
+    h.update(build_flags_text(os.path.join(CSRC, "..", "build.py")).encode())
     return h.hexdigest()[:16]
 
 

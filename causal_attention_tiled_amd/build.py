@@ -51,19 +51,29 @@ def _hipcc() -> str:
 def build(asm: bool = False, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
-    objs = []
-    for src in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(BUILD, os.path.basename(src)[:-4] + ".o") for src in srcs]
+    cmds = []
+    for src, obj in zip(srcs, objs):
         flags = [*CXXFLAGS, *EXTRA.get(os.path.basename(src), [])]
-        cmd = [hipcc, *flags, "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, cwd=BUILD)
+        cmds.append([hipcc, *flags, "-c", src, "-o", obj])
         if asm:
             s_out = os.path.join(BUILD, os.path.basename(src)[:-4] + "-gfx950.s")
-            subprocess.run([hipcc, *flags, "--cuda-device-only", "-S", src, "-o", s_out],
-                           check=True, cwd=BUILD)
-        objs.append(obj)
+            cmds.append([hipcc, *flags, "--cuda-device-only", "-S", src, "-o", s_out])
+    # the translation units are independent: compile them side by side
+    jobs = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    running, pending = [], list(cmds)
+    while pending or running:
+        while pending and len(running) < jobs:
+            cmd = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((cmd, subprocess.Popen(cmd, cwd=BUILD)))
+        cmd, proc = running.pop(0)
+        if proc.wait() != 0:
+            for _, other in running:
+                other.wait()
+            raise subprocess.CalledProcessError(proc.returncode, cmd)
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -61,6 +61,33 @@ def test_comment_edits_keep_the_hash(tmp_path, monkeypatch):
     assert b.kernel_source_hash("probe") != h0
 
 
+def test_build_flags_decide_the_hash(tmp_path, monkeypatch):
+    """Of the build script, only the compile-flag definitions enter the hash: a change in
+    how the build runs keeps it, a changed flag does not; the real script's flags are
+    found."""
+    b = _bench()
+    csrc = tmp_path / "csrc"
+    csrc.mkdir()
+    (csrc / "k.hip").write_text("int f() { return 1; }\n")
+    script = ('ARCH = "gfx950"\nCXXFLAGS = [\n    "-O3",  # optimise\n    "-g0",\n]\n'
+              '_THRESHOLD_FLAGS = ["-a", "-b"]\nEXTRA = {"k.hip": _THRESHOLD_FLAGS,\n'
+              '         "m.hip": []}\n\n\ndef build():\n    return 1\n')
+    monkeypatch.setattr(b, "CSRC", str(csrc))
+    monkeypatch.setitem(b.KERNEL_SOURCES, "probe", ["k.hip"])
+    (tmp_path / "build.py").write_text(script)
+    h0 = b.kernel_source_hash("probe")
+    (tmp_path / "build.py").write_text(script.replace("return 1", "return 2"))
+    assert b.kernel_source_hash("probe") == h0
+    for old, new in (('"-O3"', '"-O2"'), ('"-b"', '"-c"'), ('"m.hip": []', '"m.hip": ["-d"]'),
+                     ('"gfx950"', '"gfx942"')):
+        (tmp_path / "build.py").write_text(script.replace(old, new))
+        assert b.kernel_source_hash("probe") != h0, old
+    real = b.build_flags_text(os.path.join(ROOT, "causal_attention_tiled_amd", "build.py"))
+    for piece in ("ARCH =", "CXXFLAGS =", "packed-fp32-ops", "_THRESHOLD_FLAGS =", "EXTRA =",
+                  "tra_bwd.hip"):
+        assert piece in real, piece
+
+
 def test_nsa_token_counts():
     """The work counts of the NSA rows: the attended tokens of each query row match a direct
     count on a tiny case with duplicates, padding, ids past the end and a block after the
